@@ -1,0 +1,366 @@
+/*
+ * CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
+ * baseline leg of the benchmark are the only callers.  Nothing in the GPU
+ * library includes, links or calls this file, and this file includes nothing
+ * from the GPU library.
+ *
+ * Plain, slow and obviously correct: every result is the written-out
+ * definition, evaluated in IEEE binary64 with plain loops.  OpenMP only
+ * spreads independent rows / outputs over host threads; it does not change
+ * any arithmetic.
+ *
+ * Sources (all pages are about "GLM-130B: An Open Bilingual Pre-trained Model"):
+ *  [card-M]   wikillm.com paper card, section "Method", weight-only INT4
+ *             paragraph and its quantize/forward pseudocode.
+ *  [card-PvC] same card, section "Paper vs code", "Quantization scale" and
+ *             "Quantized layers" bullets.
+ *  [card-H]   same card, section "Hyperparameters" (shapes, FFN is GeGLU).
+ *  [pl-4]     paperlayer.ai summary, "INT4 Quantization for RTX 3090s/2080s"
+ *             (weights converted back to FP16 at run time, FP16 activations).
+ *  [pl-B3]    paperlayer.ai summary, section B.3 (GeGLU feed-forward).
+ * Readings of points the pages leave open are listed beside each function.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <omp.h>
+
+enum {
+    ORACLE_OK = 0,
+    ORACLE_ERR_ARG = 1,      /* NULL pointer or negative size */
+    ORACLE_ERR_NONFINITE = 2,/* a weight is NaN or Inf: the scale is undefined */
+    ORACLE_ERR_ODD_K = 3,    /* two codes per byte needs an even row length */
+    ORACLE_ERR_ROUNDING = 4  /* host FPU not in round-to-nearest-even */
+};
+
+/* ---------------------------------------------------------------------- */
+/* IEEE binary16 <-> binary64, written from the format's definition:       */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.                */
+/* ---------------------------------------------------------------------- */
+
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* zero / subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);    /* 1.f * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round a binary64 value to the nearest binary16, ties to even. */
+uint16_t oracle_double_to_half(double d)
+{
+    uint16_t sign = signbit(d) ? 0x8000 : 0;
+    double a = fabs(d);
+    if (isnan(d))
+        return (uint16_t)(sign | 0x7e00);
+    if (isinf(d))
+        return (uint16_t)(sign | 0x7c00);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: the quantum is 2^-24 everywhere */
+        double r = nearbyint(ldexp(a, 24));          /* exact scaling, then RNE */
+        return (uint16_t)(sign | (uint16_t)r);       /* r == 1024 encodes 2^-14 */
+    }
+    int e2;
+    frexp(a, &e2);                 /* a = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;                /* a in [2^E, 2^(E+1)) */
+    double r = nearbyint(ldexp(a, 10 - E));          /* significand in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return (uint16_t)(sign | 0x7c00);            /* overflow rounds to infinity */
+    return (uint16_t)(sign | ((E + 15) << 10) | ((int)r - 1024));
+}
+
+/* ---------------------------------------------------------------------- */
+/* Quantization  [card-M] [card-PvC]                                       */
+/* ---------------------------------------------------------------------- */
+
+/* One output row.  Definition, in the pages' order:
+ *   a     = max_k |W[k]|                          (row absmax)
+ *   s     = fp16(a / 7)                           (divisor 2^(b-1)-1 = 7, stored in FP16)
+ *   q[k]  = clamp(round(W[k] / s), -7, 7)         (integers in [-7, 7])
+ * Readings: round() is round-half-to-even on the exact real quotient (a
+ * binary64 quotient of two binary16 values is never far enough from a
+ * half-integer to be rounded across one, and exact ties are representable);
+ * the codes are taken against the STORED fp16 scale; a row whose scale is 0
+ * gets all-zero codes. */
+static int quantize_row(const uint16_t *w, int64_t k, int8_t *q, uint16_t *s_out)
+{
+    double a = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double v = oracle_half_to_double(w[i]);
+        if (!isfinite(v))
+            return ORACLE_ERR_NONFINITE;
+        if (fabs(v) > a)
+            a = fabs(v);
+    }
+    uint16_t s_bits = oracle_double_to_half(a / 7.0);
+    double s = oracle_half_to_double(s_bits);
+    for (int64_t i = 0; i < k; ++i) {
+        double r = 0.0;
+        if (s != 0.0) {
+            r = nearbyint(oracle_half_to_double(w[i]) / s);
+            if (r > 7.0)
+                r = 7.0;
+            if (r < -7.0)
+                r = -7.0;
+        }
+        q[i] = (int8_t)r;   /* -0.0 becomes the integer 0 */
+    }
+    *s_out = s_bits;
+    return ORACLE_OK;
+}
+
+/* Two codes per byte [card-M pseudocode comment, card-PvC "int8 packing"].
+ * Reading (the pages fix neither encoding nor order): each code is stored as
+ * its 4-bit two's complement; code 2j goes to the low nibble of byte j and
+ * code 2j+1 to the high nibble; bytes run along the input dimension, rows
+ * are output features: layout [n][k/2]. */
+static uint8_t pack_pair(int8_t lo, int8_t hi)
+{
+    return (uint8_t)(((uint8_t)lo & 0x0f) | (((uint8_t)hi & 0x0f) << 4));
+}
+
+static int8_t unpack_nibble(uint8_t byte, int high)
+{
+    int v = high ? (byte >> 4) : (byte & 0x0f);
+    return (int8_t)(v >= 8 ? v - 16 : v);
+}
+
+static int check_fe(void)
+{
+    return fegetround() == FE_TONEAREST ? ORACLE_OK : ORACLE_ERR_ROUNDING;
+}
+
+/* Codes and scales without packing (used by tests to look at q itself). */
+int oracle_quantize_codes(const uint16_t *w, int64_t n, int64_t k,
+                          int8_t *codes, uint16_t *scales)
+{
+    if (!w || !codes || !scales || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (check_fe())
+        return ORACLE_ERR_ROUNDING;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < n; ++r) {
+        int st = quantize_row(w + r * k, k, codes + r * k, scales + r);
+        if (st) {
+#pragma omp atomic write
+            status = st;
+        }
+    }
+    return status;
+}
+
+/* quantize_linear_int4 of [card-M]: W fp16 [n][k] -> packed [n][k/2], scales fp16 [n]. */
+int oracle_quantize_rowwise_int4(const uint16_t *w, int64_t n, int64_t k,
+                                 uint8_t *packed, uint16_t *scales)
+{
+    if (!w || !packed || !scales || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+    if (check_fe())
+        return ORACLE_ERR_ROUNDING;
+    int status = ORACLE_OK;
+#pragma omp parallel
+    {
+        int8_t row_stack[4096];
+        int8_t *q = row_stack;
+        int8_t *heap = NULL;
+        if (k > (int64_t)sizeof row_stack) {
+            heap = (int8_t *)malloc((size_t)k);
+            q = heap;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n; ++r) {
+            if (!q) {
+#pragma omp atomic write
+                status = ORACLE_ERR_ARG;
+                continue;
+            }
+            int st = quantize_row(w + r * k, k, q, scales + r);
+            if (st) {
+#pragma omp atomic write
+                status = st;
+                continue;
+            }
+            for (int64_t j = 0; j < k / 2; ++j)
+                packed[r * (k / 2) + j] = pack_pair(q[2 * j], q[2 * j + 1]);
+        }
+        free(heap);
+    }
+    return status;
+}
+
+/* Inverse of the packing: packed [n][k/2] -> codes int8 [n][k]. */
+int oracle_unpack_int4(const uint8_t *packed, int64_t n, int64_t k, int8_t *codes)
+{
+    if (!packed || !codes || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i)
+            codes[r * k + i] = unpack_nibble(packed[r * (k / 2) + i / 2], (int)(i & 1));
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Linear  [card-M linear_forward] [pl-4]                                  */
+/* ---------------------------------------------------------------------- */
+
+/* One output element of y = x . W_hat^T (+ bias), W_hat[n][k] = s[n] * q[n][k].
+ * In binary64 every product x * s * q is exact (11 + 11 + 3 significant
+ * bits), so the only rounding is in the K-term sum (relative ~K * 2^-53).
+ * mag = sum_k |x * W_hat| + |bias| is the scale the acceptance bound uses. */
+static void linear_one(const uint16_t *xrow, int64_t k, const uint8_t *prow,
+                       uint16_t s_bits, const uint16_t *bias_n,
+                       double *y, double *mag)
+{
+    double s = oracle_half_to_double(s_bits);
+    double acc = 0.0, m = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double wh = s * (double)unpack_nibble(prow[i / 2], (int)(i & 1));
+        double t = oracle_half_to_double(xrow[i]) * wh;
+        acc += t;
+        m += fabs(t);
+    }
+    if (bias_n) {
+        double b = oracle_half_to_double(*bias_n);
+        acc += b;
+        m += fabs(b);
+    }
+    *y = acc;
+    if (mag)
+        *mag = m;
+}
+
+/* Full output: x fp16 [m][k], packed [n][k/2], scales fp16 [n], bias fp16 [n]
+ * or NULL -> y binary64 [m][n] (not rounded to fp16), mag [m][n] or NULL. */
+int oracle_linear(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
+                  const uint16_t *scales, int64_t n, const uint16_t *bias,
+                  double *y, double *mag)
+{
+    if (!x || !packed || !scales || !y || m < 0 || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            linear_one(x + i * k, k, packed + j * (k / 2), scales[j],
+                       bias ? bias + j : NULL, y + i * n + j, mag ? mag + i * n + j : NULL);
+    return ORACLE_OK;
+}
+
+/* Selected outputs only: y[t] = y_full[mi[t]][ni[t]] (for shapes where the
+ * full product is too long for the host). */
+int oracle_linear_at(const uint16_t *x, int64_t k, const uint8_t *packed,
+                     const uint16_t *scales, const uint16_t *bias,
+                     const int64_t *mi, const int64_t *ni, int64_t count,
+                     double *y, double *mag)
+{
+    if (!x || !packed || !scales || !mi || !ni || !y || count < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < count; ++t)
+        linear_one(x + mi[t] * k, k, packed + ni[t] * (k / 2), scales[ni[t]],
+                   bias ? bias + ni[t] : NULL, y + t, mag ? mag + t : NULL);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* GeGLU  [card-H] [pl-B3]                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* GELU in its defining form t * Phi(t), Phi the standard normal CDF,
+ * Phi(t) = (1 + erf(t / sqrt 2)) / 2, with the C library's erf. */
+double oracle_gelu(double t)
+{
+    return 0.5 * t * (1.0 + erf(t / sqrt(2.0)));
+}
+
+/* g[i][j] = GELU(a[i][j]) * b[i][j], where a is the linear through weight
+ * rows [0, f) and b the linear through rows [f, 2f) of the up-projection.
+ * Reading: the first half of the rows is the GELU-gated one.  a, b and their
+ * magnitudes are returned too (each may be NULL) for the error bound. */
+int oracle_geglu(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
+                 const uint16_t *scales, int64_t f, const uint16_t *bias,
+                 double *g, double *a_out, double *b_out,
+                 double *mag_a, double *mag_b)
+{
+    if (!x || !packed || !scales || !g || m < 0 || f < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < f; ++j) {
+            double a, b, ma, mb;
+            linear_one(x + i * k, k, packed + j * (k / 2), scales[j],
+                       bias ? bias + j : NULL, &a, &ma);
+            linear_one(x + i * k, k, packed + (f + j) * (k / 2), scales[f + j],
+                       bias ? bias + f + j : NULL, &b, &mb);
+            g[i * f + j] = oracle_gelu(a) * b;
+            if (a_out) a_out[i * f + j] = a;
+            if (b_out) b_out[i * f + j] = b;
+            if (mag_a) mag_a[i * f + j] = ma;
+            if (mag_b) mag_b[i * f + j] = mb;
+        }
+    return ORACLE_OK;
+}
+
+/* Selected GeGLU outputs: column ni[t] in [0, f) of token mi[t]. */
+int oracle_geglu_at(const uint16_t *x, int64_t k, const uint8_t *packed,
+                    const uint16_t *scales, int64_t f, const uint16_t *bias,
+                    const int64_t *mi, const int64_t *ni, int64_t count,
+                    double *g, double *a_out, double *b_out,
+                    double *mag_a, double *mag_b)
+{
+    if (!x || !packed || !scales || !mi || !ni || !g || count < 0 || f < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < count; ++t) {
+        int64_t i = mi[t], j = ni[t];
+        double a, b, ma, mb;
+        linear_one(x + i * k, k, packed + j * (k / 2), scales[j],
+                   bias ? bias + j : NULL, &a, &ma);
+        linear_one(x + i * k, k, packed + (f + j) * (k / 2), scales[f + j],
+                   bias ? bias + f + j : NULL, &b, &mb);
+        g[t] = oracle_gelu(a) * b;
+        if (a_out) a_out[t] = a;
+        if (b_out) b_out[t] = b;
+        if (mag_a) mag_a[t] = ma;
+        if (mag_b) mag_b[t] = mb;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
+
+void oracle_set_num_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}

@@ -1,0 +1,295 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each test checks the oracle against an independent source: numpy's binary16
+conversion, exact rational arithmetic with a nearest-point search (not a
+division followed by rounding), closed-form invariants of the method, a
+hand-derived worked example of the layout, numpy's float64 matmul, and
+textbook values of the normal CDF.  A plausible slip anywhere in the oracle
+(wrong divisor, rounding mode, sign, nibble order, transposed operand,
+dropped term, wrong GELU form) fails at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from weight_only_int4_rowwise_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16)
+
+
+# ---------------------------------------------------------------- fp16 codec
+
+def test_half_to_double_exhaustive(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle_mod.half_to_double(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert math.copysign(1.0, ours[0x8000]) == -1.0
+
+
+def test_double_to_half_vs_numpy(oracle_mod):
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        rng.uniform(-65600, 65600, 2000),
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 70000.0, -65520.0,
+                  2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26,
+                  2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, np.inf, -np.inf]),
+    ])
+    # exact midpoints between neighbouring fp16 values: ties go to even
+    lo = np.arange(0, 0x7BFF, 37, dtype=np.uint16)
+    mids = (lo.view(np.float16).astype(np.float64) + (lo + 1).view(np.float16).astype(np.float64)) / 2
+    vals = np.concatenate([vals, mids, -mids])
+    ours = oracle_mod.double_to_half(vals)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------- scales
+
+def _nearest_fp16_exact(v: Fraction) -> int:
+    """RNE to fp16 by exact search among neighbouring representable values."""
+    guess = int(np.float16(float(v)).view(np.uint16)) & 0x7FFF
+    best = None
+    for b in range(max(0, guess - 2), min(0x7BFF, guess + 2) + 1):
+        d = abs(Fraction(float(_f16(b))) - v)
+        key = (d, b & 1)  # smaller distance first, then even significand
+        if best is None or key < best[0]:
+            best = (key, b)
+    if v > Fraction(65504) + Fraction(16):  # beyond the overflow midpoint
+        return 0x7C00
+    return best[1]
+
+
+def test_scale_exhaustive_over_all_absmax_values(oracle_mod):
+    """s = fp16(a/7) for every finite non-negative fp16 absmax a, against an
+    exact-rational nearest search (divisor 2^(b-1)-1 = 7 for b = 4)."""
+    a = synth.all_finite_nonneg_fp16().numpy()
+    w = np.stack([a, np.zeros_like(a)], axis=1)          # row [a, 0]: absmax is a
+    _, s = oracle_mod.quantize_codes(w)
+    abits = a.view(np.uint16)
+    for i in range(0, abits.size):
+        exp = _nearest_fp16_exact(Fraction(float(a[i])) / 7)
+        assert s[i] == exp, (hex(abits[i]), hex(s[i]), hex(exp))
+
+
+def test_scale_closed_form_bound(oracle_mod):
+    """|7 s - a| <= 7 * ulp(s) / 2: s is the fp16 nearest to a/7."""
+    a = synth.all_finite_nonneg_fp16().numpy()
+    w = np.stack([a, -a], axis=1)
+    _, s = oracle_mod.quantize_codes(w)
+    sv = _f16(s).astype(np.float64)
+    ulp = np.spacing(_f16(s)).astype(np.float64)
+    assert np.all(np.abs(7 * sv - a.astype(np.float64)) <= 7 * ulp / 2)
+
+
+# -------------------------------------------------------------------- codes
+
+def _nearest_code(w: Fraction, s: Fraction) -> int:
+    """argmin_j |w - s*j| over j in [-7, 7]; ties to the even j."""
+    best = None
+    for j in range(-7, 8):
+        key = (abs(w - s * j), j & 1)
+        if best is None or key < best[0]:
+            best = (key, j)
+    return best[1]
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "grid"])
+def test_codes_brute_force_nearest_point(oracle_mod, kind):
+    g = synth.generator(7)
+    if kind == "normal":
+        w = synth.weight(48, 40, g).numpy()
+    elif kind == "t4":
+        w = synth.weight(48, 40, g, "t4").numpy()
+    else:
+        w = synth.exponent_rows(48, 40, g).numpy()
+    q, s = oracle_mod.quantize_codes(w)
+    for r in range(w.shape[0]):
+        sv = Fraction(float(_f16(s[r])))
+        assert sv != 0
+        for c in range(w.shape[1]):
+            assert q[r, c] == _nearest_code(Fraction(float(w[r, c])), sv), (kind, r, c)
+
+
+def test_ties_round_to_even(oracle_mod):
+    # absmax 7 -> s = 1; entries x.5 are exact ties
+    w = np.array([[7, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5, -0.5, -1.5, -2.5, -6.5]], dtype=np.float16)
+    q, s = oracle_mod.quantize_codes(w)
+    assert s[0] == 0x3C00
+    assert q[0].tolist() == [7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -6]
+
+
+def test_code_invariants_on_workload_shaped_data(oracle_mod):
+    g = synth.generator(3)
+    for dist in ("normal", "t4"):
+        w = synth.weight(256, 1024, g, dist).numpy()
+        q, s = oracle_mod.quantize_codes(w)
+        wv = w.astype(np.float64)
+        sv = _f16(s).astype(np.float64)
+        assert q.min() >= -7 and q.max() <= 7
+        # |w - s q| <= s / 2 for every element of rows with a normal scale
+        normal = sv >= 2.0 ** -14
+        err = np.abs(wv - sv[:, None] * q)
+        assert np.all(err[normal] <= sv[normal, None] / 2)
+        # the absmax element maps to +-7
+        idx = np.abs(wv).argmax(axis=1)
+        assert np.all(np.abs(q[np.arange(len(q)), idx]) == 7)
+        # odd symmetry: q(-w) = -q(w), same scale
+        q2, s2 = oracle_mod.quantize_codes(-w)
+        assert np.array_equal(s, s2) and np.array_equal(q2, -q)
+
+
+def test_zero_and_tiny_rows(oracle_mod):
+    w = np.zeros((4, 16), dtype=np.float16)
+    w[1, 3] = _f16(1)        # 2^-24: a/7 rounds to 0
+    w[2, 5] = -_f16(3)       # 3 * 2^-24: a/7 rounds to 0
+    w[3, :] = -0.0
+    q, s = oracle_mod.quantize_codes(w)
+    assert np.all(s == 0) and np.all(q == 0)
+    p, s2 = oracle_mod.quantize_rowwise_int4(w)
+    assert np.all(p == 0) and np.all(s2 == 0)
+
+
+def test_subnormal_scale_clamps_to_seven(oracle_mod):
+    # subnormal absmax values give subnormal scales and quotients near or above 7.5
+    w = np.zeros((1, 4), dtype=np.float16)
+    w[0, 0] = _f16(11)       # 11 * 2^-24; 11/7 = 1.571 -> s = 2 * 2^-24; 11/2 = 5.5 -> 6 (even)
+    w[0, 1] = _f16(9)        # 9/2 = 4.5 -> 4 (even)
+    q, s = oracle_mod.quantize_codes(w)
+    assert s[0] == 2 and q[0].tolist() == [6, 4, 0, 0]
+    w2 = np.zeros((1, 2), dtype=np.float16)
+    w2[0, 0] = _f16(17)      # 17/7 = 2.43 -> s = 2 * 2^-24; 17/2 = 8.5 -> clamp 7
+    q2, s2 = oracle_mod.quantize_codes(w2)
+    assert s2[0] == 2 and q2[0].tolist() == [7, 0]
+
+
+# ------------------------------------------------------------------ packing
+
+def _read_golden(name):
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            d[key.strip()] = val.split()
+    return d
+
+
+def test_pack_worked_example(oracle_mod):
+    gold = _read_golden("pack_worked_example.txt")
+    w = np.array([[float(v) for v in gold["weights"]]], dtype=np.float16)
+    p, s = oracle_mod.quantize_rowwise_int4(w)
+    assert s[0] == int(gold["scale_bits"][0], 16)
+    assert p[0].tolist() == [int(b, 16) for b in gold["bytes"]]
+    assert oracle_mod.unpack_int4(p, 8)[0].tolist() == [int(c) for c in gold["codes"]]
+
+
+def test_pack_round_trip(oracle_mod):
+    g = synth.generator(5)
+    w = synth.weight(64, 256, g, "t4").numpy()
+    q, s = oracle_mod.quantize_codes(w)
+    p, s2 = oracle_mod.quantize_rowwise_int4(w)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(oracle_mod.unpack_int4(p, 256), q)
+
+
+def test_quantizer_rejects_bad_input(oracle_mod):
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.quantize_rowwise_int4(np.zeros((2, 3), dtype=np.float16))
+    w = np.zeros((2, 4), dtype=np.float16)
+    w[1, 2] = np.inf
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.quantize_rowwise_int4(w)
+
+
+# ------------------------------------------------------------------- linear
+
+def _dequant(oracle_mod, p, s, k):
+    return oracle_mod.unpack_int4(p, k).astype(np.float64) * _f16(s).astype(np.float64)[:, None]
+
+
+def test_linear_vs_numpy_float64_matmul(oracle_mod):
+    g = synth.generator(11)
+    w = synth.weight(96, 512, g).numpy()
+    x = synth.activations(5, 512, g).numpy()
+    bias = synth.normal_fp16((96,), 0.5, g).numpy()
+    p, s = oracle_mod.quantize_rowwise_int4(w)
+    wh = _dequant(oracle_mod, p, s, 512)
+    y, mag = oracle_mod.linear(x, p, s, bias)
+    ref = x.astype(np.float64) @ wh.T + bias.astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
+    refmag = np.abs(x.astype(np.float64)) @ np.abs(wh).T + np.abs(bias.astype(np.float64))
+    assert np.allclose(mag, refmag, rtol=1e-12, atol=1e-13)
+    # sampled entry points agree with the full product
+    mi = np.array([0, 4, 2, 3]); ni = np.array([0, 95, 17, 50])
+    ys, ms = oracle_mod.linear_at(x, p, s, mi, ni, bias)
+    assert np.array_equal(ys, y[mi, ni]) and np.array_equal(ms, mag[mi, ni])
+
+
+def test_linear_one_hot_is_scaled_code(oracle_mod):
+    g = synth.generator(12)
+    w = synth.weight(40, 64, g, "t4").numpy()
+    q, s = oracle_mod.quantize_codes(w)
+    p, _ = oracle_mod.quantize_rowwise_int4(w)
+    cols = list(range(64))
+    x = synth.one_hot_activations(cols, 64).numpy()
+    y, _ = oracle_mod.linear(x, p, s)
+    assert np.array_equal(y, (q.astype(np.float64) * _f16(s).astype(np.float64)[:, None]).T)
+
+
+# -------------------------------------------------------------------- GeGLU
+
+def test_gelu_textbook_values(oracle_mod):
+    with open(os.path.join(GOLDEN, "gelu_values.txt")) as fh:
+        rows = [l.split() for l in fh if l.strip() and not l.startswith("#")]
+    for t, phi in rows:
+        t, phi = float(t), float(phi)
+        assert oracle_mod.gelu(t) == pytest.approx(t * phi, rel=1e-13, abs=1e-300)
+
+
+def test_gelu_identities_and_scipy(oracle_mod):
+    from scipy.stats import norm
+    ts = np.linspace(-8, 8, 321)
+    for t in ts:
+        gt = oracle_mod.gelu(t)
+        assert gt - oracle_mod.gelu(-t) == pytest.approx(t, abs=1e-14)
+        assert gt == pytest.approx(t * norm.cdf(t), rel=1e-12, abs=1e-15)
+    assert oracle_mod.gelu(0.0) == 0.0
+    # derivative at 0 is Phi(0) = 1/2; erf form, not the tanh approximation (differs at -3)
+    assert (oracle_mod.gelu(1e-6) - oracle_mod.gelu(-1e-6)) / 2e-6 == pytest.approx(0.5, rel=1e-9)
+    tanh_form = 0.5 * -3 * (1 + math.tanh(math.sqrt(2 / math.pi) * (-3 + 0.044715 * -27)))
+    assert abs(oracle_mod.gelu(-3.0) - tanh_form) > 1e-4
+
+
+def test_geglu_vs_numpy_halves(oracle_mod):
+    from scipy.stats import norm
+    g = synth.generator(13)
+    f, k = 48, 256
+    w = synth.weight(2 * f, k, g, "t4").numpy()
+    x = synth.activations(3, k, g).numpy()
+    p, s = oracle_mod.quantize_rowwise_int4(w)
+    wh = _dequant(oracle_mod, p, s, k)
+    a = x.astype(np.float64) @ wh[:f].T
+    b = x.astype(np.float64) @ wh[f:].T
+    gg, aa, bb, ma, mb = oracle_mod.geglu(x, p, s)
+    assert np.allclose(aa, a, rtol=1e-12, atol=1e-13)
+    assert np.allclose(bb, b, rtol=1e-12, atol=1e-13)
+    assert np.allclose(gg, a * norm.cdf(a) * b, rtol=1e-11, atol=1e-13)
+    mi = np.array([0, 2, 1]); ni = np.array([0, 47, 20])
+    gs = oracle_mod.geglu_at(x, p, s, mi, ni)
+    assert np.array_equal(gs[0], gg[mi, ni])

@@ -1,0 +1,169 @@
+"""Seeded synthetic inputs at GLM-130B shapes.
+
+This module only draws and arranges numbers.  It holds none of the
+quantization or matmul arithmetic, so both the GPU path and the CPU oracle can
+be fed from it without sharing any of the method's code.
+
+Recipe (one ``torch.Generator`` per workload, seed 0 unless stated; weights
+are drawn before activations):
+
+* N(0, sigma^2) values: ``randn`` in float32, times sigma, rounded to fp16.
+* Student-t(nu=4) * scale: Z0 / sqrt((Z1^2 + Z2^2 + Z3^2 + Z4^2) / 4) * scale
+  from five successive ``randn`` draws, rounded to fp16 (heavy tails that
+  stress the row absmax).
+* Activations: N(0, 1) in fp16.
+
+Shapes are GLM-130B's (GLM-130B paper card, "Method" and "Hyperparameters"):
+hidden 12288, 96 heads of 128, FFN width 32768 (GeGLU, so the up-projection
+has 2 x 32768 output rows), 70 layers, sequence length 2048.
+"""
+from __future__ import annotations
+
+import torch
+
+HIDDEN = 12288
+FFN = 32768
+LAYERS = 70
+SEQ = 2048
+QKV_OUT = 3 * HIDDEN
+
+# (name, out_features, in_features) of the four quantized linears of a layer
+# (QKV projection, attention output, GeGLU up-projection, down-projection).
+LAYER_LINEARS = (
+    ("qkv", QKV_OUT, HIDDEN),
+    ("attn_out", HIDDEN, HIDDEN),
+    ("ffn_up", 2 * FFN, HIDDEN),
+    ("ffn_down", HIDDEN, FFN),
+)
+
+
+def generator(seed: int = 0, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal_fp16(shape, sigma: float, gen: torch.Generator, device: str = "cpu") -> torch.Tensor:
+    t = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    return t.to(torch.float16)
+
+
+def student_t4_fp16(shape, scale: float, gen: torch.Generator, device: str = "cpu") -> torch.Tensor:
+    z0 = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+    chi = torch.zeros(*shape, dtype=torch.float32, device=device)
+    for _ in range(4):
+        z = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+        chi.addcmul_(z, z)
+    return (z0 / torch.sqrt(chi / 4.0) * scale).to(torch.float16)
+
+
+def weight(n: int, k: int, gen: torch.Generator, dist: str = "normal", device: str = "cpu") -> torch.Tensor:
+    """FP16 weight [n][k] (out x in): 'normal' = N(0, 0.02^2), 't4' = t(4) * 0.02."""
+    if dist == "normal":
+        return normal_fp16((n, k), 0.02, gen, device)
+    if dist == "t4":
+        return student_t4_fp16((n, k), 0.02, gen, device)
+    raise ValueError(dist)
+
+
+def activations(m: int, k: int, gen: torch.Generator, device: str = "cpu") -> torch.Tensor:
+    return normal_fp16((m, k), 1.0, gen, device)
+
+
+# ---------------------------------------------------------------------------
+# Workloads (each returns CPU fp16 tensors; the caller moves them)
+# ---------------------------------------------------------------------------
+
+def toy(seed: int = 0):
+    """Weight 1024 x 1024 ~ N(0, 0.02^2); activations for M = 1 and M = 16."""
+    g = generator(seed)
+    w = weight(1024, 1024, g)
+    x1 = activations(1, 1024, g)
+    x16 = activations(16, 1024, g)
+    return w, {1: x1, 16: x16}
+
+
+def qkv_decode(ms=(1, 8, 32, 64), seed: int = 0):
+    """QKV projection 36864 x 12288 ~ N(0, 0.02^2); activations per M."""
+    g = generator(seed)
+    w = weight(QKV_OUT, HIDDEN, g)
+    return w, {m: activations(m, HIDDEN, g) for m in ms}
+
+
+def geglu_decode(ms=(1, 16), seed: int = 0):
+    """GeGLU up 65536 x 12288 and down 12288 x 32768, t(4) * 0.02 weights."""
+    g = generator(seed)
+    w_up = weight(2 * FFN, HIDDEN, g, "t4")
+    w_down = weight(HIDDEN, FFN, g, "t4")
+    x_up = {m: activations(m, HIDDEN, g) for m in ms}
+    x_down = {m: activations(m, FFN, g) for m in ms}
+    return w_up, w_down, x_up, x_down
+
+
+def prefill(seed: int = 0, m: int = SEQ):
+    """Attention-out 12288 x 12288 and FFN-up 65536 x 12288 ~ N(0, 0.02^2); M = 2048."""
+    g = generator(seed)
+    w_attn = weight(HIDDEN, HIDDEN, g)
+    w_up = weight(2 * FFN, HIDDEN, g)
+    x = activations(m, HIDDEN, g)
+    return w_attn, w_up, x
+
+
+def layer_weight_seed(layer: int, matrix_id: int) -> int:
+    """Seed of one matrix of the full-model decode step (drawn on the device)."""
+    return 1000 * layer + matrix_id
+
+
+# ---------------------------------------------------------------------------
+# Structured inputs for exact tests (bit patterns only, no method arithmetic)
+# ---------------------------------------------------------------------------
+
+def all_finite_nonneg_fp16() -> torch.Tensor:
+    """Every finite non-negative fp16 value, +0 .. 65504 (31744 values)."""
+    return torch.arange(0, 0x7C00, dtype=torch.int32).to(torch.int16).view(torch.float16)
+
+
+def enumeration_rows(absmax_bits, k: int) -> torch.Tensor:
+    """One row per absmax bit pattern a: the row holds +a, then every fp16
+    value v with 0 < |v| <= a in both signs, in increasing bit order, repeated
+    cyclically to fill k entries.  Every (absmax, weight) pair that can occur
+    in a row with that absmax appears once per row if k is large enough."""
+    rows = []
+    for a in absmax_bits:
+        a = int(a)
+        pos = torch.arange(1, a + 1, dtype=torch.int32)
+        vals = torch.cat([pos, pos | 0x8000]) if a > 0 else torch.zeros(0, dtype=torch.int32)
+        body = torch.cat([torch.tensor([a], dtype=torch.int32), vals])
+        reps = -(-k // body.numel())
+        row = body.repeat(reps)[:k]
+        rows.append(row)
+    bits = torch.stack(rows).to(torch.int32)
+    bits = torch.where(bits >= 0x8000, bits - 0x10000, bits).to(torch.int16)
+    return bits.view(torch.float16)
+
+
+def exponent_rows(n: int, k: int, gen: torch.Generator, e_lo: int = -8, e_hi: int = 0) -> torch.Tensor:
+    """Rows whose absmax is 7 * 2^e (e drawn in [e_lo, e_hi]), with every
+    other entry an integer j * 2^e or (j + 1/2) * 2^e, |j| <= 6: exact
+    power-of-two grids that hit every rounding tie."""
+    e = torch.randint(e_lo, e_hi + 1, (n, 1), generator=gen)
+    half_steps = torch.randint(-13, 14, (n, k), generator=gen).to(torch.float64)
+    vals = half_steps * 0.5 * torch.pow(2.0, e.to(torch.float64))
+    col = torch.randint(0, k, (n,), generator=gen)
+    sign = torch.where(torch.rand(n, generator=gen) < 0.5, -1.0, 1.0).to(torch.float64)
+    vals[torch.arange(n), col] = 7.0 * torch.pow(2.0, e[:, 0].to(torch.float64)) * sign
+    return vals.to(torch.float16)
+
+
+def small_int_activations(m: int, k: int, gen: torch.Generator, lo: int = -3, hi: int = 3) -> torch.Tensor:
+    """Integer-valued fp16 activations in [lo, hi]."""
+    return torch.randint(lo, hi + 1, (m, k), generator=gen).to(torch.float16)
+
+
+def one_hot_activations(cols, k: int) -> torch.Tensor:
+    """Row t is the unit vector e_{cols[t]} of length k."""
+    x = torch.zeros(len(cols), k, dtype=torch.float16)
+    x[torch.arange(len(cols)), torch.as_tensor(cols)] = 1.0
+    return x
