@@ -1,0 +1,138 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) weight-only INT4 row-wise library.
+ *
+ * The method (GLM-130B, "GLM-130B: An Open Bilingual Pre-trained Model"):
+ * every FP16 weight matrix of a linear layer, laid out [out_features][in_features],
+ * is quantized with one absmax scale per output row, s = fp16(max|W[n,:]| / 7),
+ * to integer codes q = clamp(round(W / s), -7, 7) packed two per byte; at run
+ * time the FP16 activations multiply the dequantized weights s * q.
+ *   - wikillm.com paper card, section "Method": weight-only INT4 paragraph and
+ *     the quantize_linear_int4 / linear_forward pseudocode;
+ *   - same card, section "Paper vs code", bullet "Quantization scale": divisor
+ *     2^(b-1) - 1 = 7, computed per output row in FP16, then rounding and
+ *     int8 packing; bullet "Quantized layers": QKV, attention output and both
+ *     MLP projections are quantized, biases stay FP16;
+ *   - same card, "Hyperparameters": hidden 12288, FFN 32768 (GeGLU);
+ *   - paperlayer.ai summary, "INT4 Quantization for RTX 3090s/2080s": FP16
+ *     activations, weights turned back into FP16 at run time.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
+ *    row-major and contiguous, and must be 16-byte aligned.
+ *  - fp16 means IEEE binary16.  Packed weights are uint8 [n][k/2]: code
+ *    q[n][2j] is the low nibble and q[n][2j+1] the high nibble of byte
+ *    [n][j], each as 4-bit two's complement (the pages fix neither order nor
+ *    encoding; this is the plainest reading).  Codes are in [-7, 7].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work: they return before the GPU finishes, and a fault inside a
+ *    kernel surfaces at the caller's next synchronisation.
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device or host memory, keeps no pointer after returning, and has no
+ *    mutable global state apart from a per-thread last-error string: calls
+ *    are reentrant and thread-safe.
+ *  - Errors: every argument is checked before any HIP call; on a failed
+ *    check nothing is enqueued and no memory is touched.  After the launch
+ *    hipGetLastError() is read; a launch failure returns W4A16_ERR_HIP and
+ *    w4a16_last_error() (per thread) names the HIP error.
+ *  - Outputs must not overlap inputs.  Sizes are element counts.
+ *  - Sizes are checked first.  m == 0 or n == 0 (f == 0) is then a valid
+ *    empty call: nothing is launched and the pointers are not looked at
+ *    (they may be NULL).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,   /* a required pointer is NULL */
+    W4A16_ERR_SHAPE = 2,  /* a size is negative, k is 0, k violates the
+                             divisibility rule of the call, or a size is too large */
+    W4A16_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
+    W4A16_ERR_HIP = 4,    /* the HIP runtime reported an error (see w4a16_last_error) */
+    W4A16_ERR_DEVICE = 5  /* no code object for the current device (it is not gfx950) */
+} w4a16_status;
+
+#define W4A16_ABI_VERSION 1
+
+/*
+ * quantize_rowwise_int4 -- quantize_linear_int4 of the paper card ("Method").
+ *
+ *   w_fp16      in   fp16  [n][k]    weight, out_features x in_features
+ *   n, k             n >= 0, k >= 2, k even
+ *   q_packed    out  uint8 [n][k/2]  packed codes (layout above)
+ *   scales_fp16 out  fp16  [n]       s[r] = fp16_rne(max_c |w[r][c]| / 7)
+ *
+ * Codes are round-half-to-even of the exact quotient w / s (against the
+ * STORED fp16 scale), clamped to [-7, 7]; a row whose scale rounds to 0
+ * (all-zero rows, or absmax <= 3 * 2^-24) gets s = 0 and all-zero codes.
+ * Weights must be finite; for NaN or Inf inputs the outputs are unspecified.
+ * The result is bit-for-bit deterministic.
+ */
+w4a16_status quantize_rowwise_int4(const void *w_fp16, int64_t n, int64_t k,
+                                   void *q_packed, void *scales_fp16, void *stream);
+
+/*
+ * w4a16_linear -- linear_forward of the paper card ("Method"), W4A16:
+ *   y[i][r] = fp16_rne( s[r] * sum_c x[i][c] * q[r][c]  (+ bias[r]) )
+ * accumulated in fp32; the scale is applied once per output after the sum
+ * (it is constant along the reduced dimension), the bias (if any) is added
+ * in fp32, and there is one rounding to fp16.
+ *
+ *   x_fp16      in   fp16  [m][k]    activations (tokens x in_features)
+ *   m, k             m >= 0, k > 0, k % 32 == 0
+ *   q_packed    in   uint8 [n][k/2]  from quantize_rowwise_int4
+ *   scales_fp16 in   fp16  [n]
+ *   n                n >= 0
+ *   bias_fp16   in   fp16  [n] or NULL
+ *   y_fp16      out  fp16  [m][n]
+ *
+ * m <= 64 runs the memory-bound decode kernel; larger m the MFMA GEMM.
+ * Results are deterministic (no atomics, fixed reduction order).
+ */
+w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k,
+                          const void *q_packed, const void *scales_fp16, int64_t n,
+                          const void *bias_fp16, void *y_fp16, void *stream);
+
+/*
+ * w4a16_geglu_linear -- the GeGLU up-projection of the FFN (paper card,
+ * "Method" and "Hyperparameters"; paperlayer.ai summary, section B.3) fused
+ * into the W4A16 linear:
+ *   a[i][j] = linear through weight rows j        (j in [0, f))
+ *   b[i][j] = linear through weight rows f + j
+ *   y[i][j] = fp16_rne( GELU(a) * b ),  GELU(t) = t * Phi(t) (erf form)
+ * where a and b are kept in fp32 (scale and bias applied) until the single
+ * final rounding.  The pages do not say which half is gated; the first f
+ * rows are taken as the GELU branch.
+ *
+ *   x_fp16      in   fp16  [m][k]      m >= 0, k > 0, k % 32 == 0
+ *   q_packed    in   uint8 [2f][k/2]
+ *   scales_fp16 in   fp16  [2f]
+ *   f                f >= 0 (output width)
+ *   bias_fp16   in   fp16  [2f] or NULL
+ *   y_fp16      out  fp16  [m][f]
+ */
+w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k,
+                                const void *q_packed, const void *scales_fp16, int64_t f,
+                                const void *bias_fp16, void *y_fp16, void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *w4a16_status_string(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *w4a16_last_error(void);
+
+/* W4A16_ABI_VERSION of the built library. */
+int w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

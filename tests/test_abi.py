@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports what include/w4a16.h declares, and
+rejects bad arguments before touching any device (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_only_int4_rowwise_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libw4a16.so not built (python -m weight_only_int4_rowwise_amd.build)")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == set(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.w4a16_abi_version() == _lib.ABI_VERSION
+    for st in range(6):
+        s = lib.w4a16_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.w4a16_status_string(99).decode() == "unknown status"
+    assert lib.w4a16_last_error() is not None
+
+
+# Fake device addresses: never dereferenced, because every call below is
+# rejected (or is empty) before the library makes any HIP call.
+A = 0x10000          # 16-byte aligned
+B = 0x20000
+C = 0x30000
+D = 0x40000
+MIS = 0x10008        # 8-byte aligned only
+
+
+def test_quantize_argument_checks(lib):
+    q = lib.quantize_rowwise_int4
+    assert q(None, 4, 32, B, C, None) == _lib.ERR_NULL
+    assert q(A, 4, 32, None, C, None) == _lib.ERR_NULL
+    assert q(A, 4, 32, B, None, None) == _lib.ERR_NULL
+    assert q(A, -1, 32, B, C, None) == _lib.ERR_SHAPE
+    assert q(A, 4, 0, B, C, None) == _lib.ERR_SHAPE
+    assert q(A, 4, 33, B, C, None) == _lib.ERR_SHAPE      # two codes per byte needs even k
+    assert q(A, 1 << 31, 32, B, C, None) == _lib.ERR_SHAPE
+    assert q(MIS, 4, 32, B, C, None) == _lib.ERR_ALIGN
+    assert q(A, 4, 32, MIS, C, None) == _lib.ERR_ALIGN
+    assert q(A, 0, 32, B, C, None) == _lib.OK            # empty: nothing launched
+    assert q(None, 0, 32, None, None, None) == _lib.OK   # empty: pointers not looked at
+
+
+@pytest.mark.parametrize("fn", ["w4a16_linear", "w4a16_geglu_linear"])
+def test_linear_argument_checks(lib, fn):
+    f = getattr(lib, fn)
+    assert f(None, 1, 64, B, C, 16, None, D, None) == _lib.ERR_NULL
+    assert f(A, 1, 64, None, C, 16, None, D, None) == _lib.ERR_NULL
+    assert f(A, 1, 64, B, None, 16, None, D, None) == _lib.ERR_NULL
+    assert f(A, 1, 64, B, C, 16, None, None, None) == _lib.ERR_NULL
+    assert f(A, -1, 64, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 0, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 48, B, C, 16, None, D, None) == _lib.ERR_SHAPE   # k % 32 != 0
+    assert f(A, 1, 64, B, C, -2, None, D, None) == _lib.ERR_SHAPE
+    assert f(A, 1 << 31, 64, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+    assert f(MIS, 1, 64, B, C, 16, None, D, None) == _lib.ERR_ALIGN
+    assert f(A, 1, 64, B, C, 16, MIS, D, None) == _lib.ERR_ALIGN     # bias
+    assert f(A, 1, 64, B, C, 16, None, MIS, None) == _lib.ERR_ALIGN
+    assert f(A, 0, 64, B, C, 16, None, D, None) == _lib.OK           # empty
+    assert f(A, 3, 64, B, C, 0, None, D, None) == _lib.OK            # empty
+    assert f(None, 0, 64, None, None, 16, None, None, None) == _lib.OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import weight_only_int4_rowwise_amd as w4
+    w = torch.zeros(4, 32, dtype=torch.float16)
+    with pytest.raises(ValueError, match="no CPU path"):
+        w4.quantize_rowwise_int4(w)

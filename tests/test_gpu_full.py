@@ -1,0 +1,160 @@
+"""GPU parity at the full GLM-130B shapes, in the launch configurations the
+benchmark times.
+
+Inputs are drawn on the GPU (seeded ``torch.Generator('cuda')``; the same
+tensors are copied to the host for the oracle).  Quantized bytes and scales
+are compared in full; decode outputs (m <= 64) in full; prefill outputs
+(m = 2048) on sampled rows and columns that touch every output tile.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_int4_rowwise_amd as w4
+from weight_only_int4_rowwise_amd import synth
+
+from helpers import announce, assert_bits_equal, assert_within, bits, f64, u8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4.library()
+    oracle._load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _quantize_checked(w, what):
+    announce("quantize", what, tuple(w.shape))
+    q, s = w4.quantize_rowwise_int4(w)
+    torch.cuda.synchronize()
+    p_ref, s_ref = oracle.quantize_rowwise_int4(bits(w))
+    assert_bits_equal(bits(s), s_ref, f"{what}: scales")
+    assert_bits_equal(u8(q), p_ref, f"{what}: packed")
+    return q, s, p_ref, s_ref
+
+
+@pytest.fixture(scope="module")
+def qkv():
+    w, xs = synth.qkv_decode(device=DEV)
+    q, s, p_ref, s_ref = _quantize_checked(w, "QKV 36864x12288")
+    del w
+    return q, s, p_ref, s_ref, xs
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_qkv_decode_full(qkv, m):
+    q, s, p_ref, s_ref, xs = qkv
+    x = xs[m]
+    announce("QKV decode", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
+    r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
+    print(f"QKV M={m}: max err/bound {r:.4f}")
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    w_up, w_down, x_up, x_down = synth.geglu_decode(device=DEV)
+    up = _quantize_checked(w_up, "FFN up 65536x12288 t4")
+    del w_up
+    down = _quantize_checked(w_down, "FFN down 12288x32768 t4")
+    del w_down
+    return up, down, x_up, x_down
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_geglu_decode_full(ffn, m):
+    (q, s, p_ref, s_ref), _, x_up, _ = ffn
+    x = x_up[m]
+    announce("GeGLU up decode", m)
+    y = w4.w4a16_geglu_linear(x, q, s)
+    torch.cuda.synchronize()
+    g, a, b, ma, mb = oracle.geglu(bits(x), p_ref, s_ref)
+    r = assert_within(f64(y), g, oracle.geglu_bound(g, a, b, ma, mb), f"GeGLU up M={m}")
+    print(f"GeGLU up M={m}: max err/bound {r:.4f}")
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_down_decode_full(ffn, m):
+    _, (q, s, p_ref, s_ref), _, x_down = ffn
+    x = x_down[m]
+    announce("FFN down decode", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
+    r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"down M={m}")
+    print(f"down M={m}: max err/bound {r:.4f}")
+
+
+def _gather(y, mi, ni):
+    """y[mi[t], ni[t]] taken on the device (the full output is large)."""
+    return y[torch.as_tensor(mi, device=y.device), torch.as_tensor(ni, device=y.device)].double().cpu().numpy()
+
+
+def _sample_indices(m, n, tile_m, tile_n, seed):
+    """One random token row in every token tile and two random columns in
+    every output tile; returns (rows, cols) of the sampled outputs."""
+    rng = np.random.default_rng(seed)
+    rows = np.array([min(m - 1, t + rng.integers(tile_m)) for t in range(0, m, tile_m)])
+    cols = np.concatenate([rng.integers(t, min(n, t + tile_n), 2) for t in range(0, n, tile_n)])
+    cols = np.unique(cols)
+    mi = np.concatenate([np.repeat(rows, n), np.tile(np.arange(m), cols.size)])
+    ni = np.concatenate([np.tile(np.arange(n), rows.size), np.repeat(cols, m)])
+    return mi, ni
+
+
+@pytest.fixture(scope="module")
+def prefill_data():
+    w_attn, w_up, x = synth.prefill(device=DEV)
+    attn = _quantize_checked(w_attn, "attn-out 12288x12288")
+    del w_attn
+    up = _quantize_checked(w_up, "FFN up 65536x12288")
+    del w_up
+    return attn, up, x
+
+
+def test_prefill_attn_out_sampled(prefill_data):
+    (q, s, p_ref, s_ref), _, x = prefill_data
+    announce("prefill attn-out", tuple(x.shape))
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(x.shape[0], q.shape[0], 128, 128, 1)
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    yg = _gather(y, mi, ni)
+    r = assert_within(yg, y_ref, oracle.linear_bound(mag), "prefill attn-out")
+    print(f"prefill attn-out: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
+def test_prefill_ffn_up_geglu_sampled(prefill_data):
+    _, (q, s, p_ref, s_ref), x = prefill_data
+    announce("prefill FFN-up GeGLU", tuple(x.shape))
+    y = w4.w4a16_geglu_linear(x, q, s)
+    torch.cuda.synchronize()
+    f = q.shape[0] // 2
+    mi, ni = _sample_indices(x.shape[0], f, 128, 64, 2)
+    g, a, b, ma, mb = oracle.geglu_at(bits(x), p_ref, s_ref, mi, ni)
+    yg = _gather(y, mi, ni)
+    r = assert_within(yg, g, oracle.geglu_bound(g, a, b, ma, mb), "prefill FFN-up GeGLU")
+    print(f"prefill FFN-up GeGLU: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
+def test_prefill_ffn_up_plain_sampled(prefill_data):
+    _, (q, s, p_ref, s_ref), x = prefill_data
+    announce("prefill FFN-up plain", tuple(x.shape))
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(x.shape[0], q.shape[0], 128, 128, 3)
+    keep = np.random.default_rng(4).random(mi.size) < 0.25     # a quarter of the sample
+    mi, ni = mi[keep], ni[keep]
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "prefill FFN-up plain")
+    print(f"prefill FFN-up plain: {mi.size} sampled outputs, max err/bound {r:.4f}")

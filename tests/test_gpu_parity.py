@@ -1,0 +1,273 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Quantized bytes and scales must be bit-exact.  Linear outputs must satisfy
+|y - y_ref| <= 2e-3 * sum_k |x_k w_hat_k| (+|bias|) + 1e-4, GeGLU outputs the
+propagated bound of oracle.geglu_bound; structural cases whose exact result
+is a single rounding (one-hot activations, power-of-two scales with integer
+activations) must be bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_int4_rowwise_amd as w4
+from weight_only_int4_rowwise_amd import synth
+
+from helpers import announce, assert_bits_equal, assert_within, bits, f64, u8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4.library()
+    oracle._load()
+    yield
+    torch.cuda.synchronize()
+
+
+def quantize_both(w_cpu: torch.Tensor, what: str):
+    announce("quantize", what, tuple(w_cpu.shape))
+    q, s = w4.quantize_rowwise_int4(w_cpu.to(DEV))
+    torch.cuda.synchronize()
+    p_ref, s_ref = oracle.quantize_rowwise_int4(bits(w_cpu))
+    assert_bits_equal(bits(s), s_ref, f"{what}: scales")
+    assert_bits_equal(u8(q), p_ref, f"{what}: packed codes")
+    return q, s, p_ref, s_ref
+
+
+def check_linear(x_cpu, q, s, p_ref, s_ref, what, bias_cpu=None):
+    announce("linear", what, tuple(x_cpu.shape), tuple(q.shape))
+    y = w4.w4a16_linear(x_cpu.to(DEV), q, s, None if bias_cpu is None else bias_cpu.to(DEV))
+    torch.cuda.synchronize()
+    y_ref, mag = oracle.linear(bits(x_cpu), p_ref, s_ref, None if bias_cpu is None else bits(bias_cpu))
+    return assert_within(f64(y), y_ref, oracle.linear_bound(mag), what)
+
+
+def check_geglu(x_cpu, q, s, p_ref, s_ref, what, bias_cpu=None):
+    announce("geglu", what, tuple(x_cpu.shape), tuple(q.shape))
+    y = w4.w4a16_geglu_linear(x_cpu.to(DEV), q, s, None if bias_cpu is None else bias_cpu.to(DEV))
+    torch.cuda.synchronize()
+    g, a, b, ma, mb = oracle.geglu(bits(x_cpu), p_ref, s_ref, None if bias_cpu is None else bits(bias_cpu))
+    return assert_within(f64(y), g, oracle.geglu_bound(g, a, b, ma, mb), what)
+
+
+# ------------------------------------------------------------------ quantizer
+
+def test_quantize_toy_bit_exact():
+    w, _ = synth.toy()
+    quantize_both(w, "toy 1024x1024")
+
+
+def test_quantize_every_absmax_and_weight_pair():
+    """All 31744 finite non-negative fp16 absmax values a; each row holds
+    every fp16 weight of magnitude <= a, in both signs (row length >= 2a+1,
+    so the first batch runs the register path, the others the two-sweep
+    path)."""
+    all_a = torch.arange(0, 0x7C00)
+    for start in range(0, all_a.numel(), 4096):
+        a = all_a[start:start + 4096]
+        k = (2 * int(a[-1]) + 1 + 7) // 8 * 8
+        w = synth.enumeration_rows(a, k)
+        quantize_both(w, f"enumeration absmax {start}..{start + a.numel() - 1} k={k}")
+
+
+@pytest.mark.parametrize("k", [12288, 1000, 4096, 2, 30, 65538])
+def test_quantize_ties_and_paths(k):
+    """Power-of-two grids full of exact ties; k picks the register path
+    (k % 8 == 0, k <= 32768) or the two-sweep path."""
+    g = synth.generator(21)
+    w = synth.exponent_rows(300, k, g)
+    quantize_both(w, f"ties k={k}")
+
+
+def test_quantize_zero_tiny_and_signed_zero_rows():
+    w = torch.zeros(6, 256, dtype=torch.float16)
+    w[1, 7] = torch.tensor([1], dtype=torch.int16).view(torch.float16)          # 2^-24
+    w[2, 9] = -torch.tensor([3], dtype=torch.int16).view(torch.float16)         # -3 * 2^-24
+    w[3] = -0.0
+    w[4, 100] = torch.tensor([11], dtype=torch.int16).view(torch.float16)       # subnormal scale
+    w[5, :] = torch.tensor([17], dtype=torch.int16).view(torch.float16)         # a/s > 7.5 -> clamp
+    _, s, _, s_ref = quantize_both(w, "zero/tiny rows")
+    assert (bits(s)[:4] == 0).all()
+
+
+# ------------------------------------------------------------ decode linear
+
+def test_toy_linear_m1_m16_with_and_without_bias():
+    w, xs = synth.toy()
+    q, s, p_ref, s_ref = quantize_both(w, "toy")
+    g = synth.generator(1)
+    bias = synth.normal_fp16((1024,), 0.5, g)
+    for m, x in xs.items():
+        check_linear(x, q, s, p_ref, s_ref, f"toy M={m}")
+        check_linear(x, q, s, p_ref, s_ref, f"toy M={m} bias", bias)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 13, 16, 17, 24, 31, 32, 33, 40, 48, 49, 63, 64])
+def test_decode_ragged_shapes(m):
+    """m across all four 16-token blocks; n not a multiple of any tile; k a
+    multiple of 32 but not of 128 (partial last reduction step)."""
+    g = synth.generator(100 + m)
+    w = synth.weight(1000, 1120, g, "t4")
+    x = synth.activations(m, 1120, g)
+    bias = synth.normal_fp16((1000,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"ragged m={m}")
+    check_linear(x, q, s, p_ref, s_ref, f"ragged m={m}")
+    check_linear(x, q, s, p_ref, s_ref, f"ragged m={m} bias", bias)
+
+
+@pytest.mark.parametrize("k", [32, 64, 96, 160])
+def test_decode_short_reduction(k):
+    g = synth.generator(7 + k)
+    w = synth.weight(77, k, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"short k={k}")
+    for m in (1, 7, 64):
+        check_linear(synth.activations(m, k, g), q, s, p_ref, s_ref, f"short k={k} m={m}")
+
+
+def _one_hot_case(m, n, k, seed):
+    g = synth.generator(seed)
+    w = synth.weight(n, k, g, "t4")
+    q, s, p_ref, s_ref = quantize_both(w, f"one-hot n={n} k={k}")
+    cols = torch.randint(0, k, (m,), generator=g).tolist()
+    x = synth.one_hot_activations(cols, k)
+    announce("one-hot linear", m, n, k)
+    y = w4.w4a16_linear(x.to(DEV), q, s)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.linear(bits(x), p_ref, s_ref)
+    # a single product s * q: its fp16 rounding is the only rounding
+    assert_bits_equal(bits(y), oracle.double_to_half(y_ref.ravel()).reshape(y_ref.shape), f"one-hot m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 37, 64])
+def test_decode_one_hot_bit_exact(m):
+    _one_hot_case(m, 530, 4096, 300 + m)
+
+
+def _pow2_case(m, n, k, seed):
+    g = synth.generator(seed)
+    w = synth.exponent_rows(n, k, g, -6, 0)
+    q, s, p_ref, s_ref = quantize_both(w, f"pow2 n={n} k={k}")
+    x = synth.small_int_activations(m, k, g)
+    announce("pow2 linear", m, n, k)
+    y = w4.w4a16_linear(x.to(DEV), q, s)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.linear(bits(x), p_ref, s_ref)
+    # integer sums are exact in fp32 and s = 2^e: one rounding to fp16
+    assert_bits_equal(bits(y), oracle.double_to_half(y_ref.ravel()).reshape(y_ref.shape), f"pow2 m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 9, 16, 50, 64])
+def test_decode_pow2_scales_bit_exact(m):
+    _pow2_case(m, 700, 2048, 400 + m)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 33, 64])
+def test_decode_geglu_small(m):
+    g = synth.generator(500 + m)
+    f, k = 500, 1056
+    w = synth.weight(2 * f, k, g, "t4")
+    q, s, p_ref, s_ref = quantize_both(w, f"geglu f={f}")
+    x = synth.activations(m, k, g)
+    check_geglu(x, q, s, p_ref, s_ref, f"geglu m={m}")
+    bias = synth.normal_fp16((2 * f,), 0.5, g)
+    check_geglu(x, q, s, p_ref, s_ref, f"geglu m={m} bias", bias)
+
+
+def test_geglu_negative_gate_region_distinguishes_erf_from_tanh():
+    """Gate pre-activations near -3 where the erf and tanh GELU differ by
+    ~10% relative: the fused output must follow the erf form."""
+    f, k = 64, 256
+    w = torch.zeros(2 * f, k, dtype=torch.float16)
+    w[:f, 0] = 7.0 * 2.0 ** -2                   # gate rows: s = 2^-2, code 7 at k=0
+    w[f:, 1] = 7.0                               # value rows: s = 1, code 7 at k=1
+    q, s, p_ref, s_ref = quantize_both(w, "erf gate")
+    x = torch.zeros(3, k, dtype=torch.float16)
+    x[:, 0] = torch.tensor([-1.75, -1.5, -2.0], dtype=torch.float16)   # a = 7/4 * x0
+    x[:, 1] = 1.0 / 7.0                                                # b ~= 1
+    y = w4.w4a16_geglu_linear(x.to(DEV), q, s)
+    torch.cuda.synchronize()
+    g, a, b, ma, mb = oracle.geglu(bits(x), p_ref, s_ref)
+    assert_within(f64(y), g, oracle.geglu_bound(g, a, b, ma, mb), "erf gate")
+    assert np.all(np.abs(f64(y) - g) <= 2e-3 * np.abs(g) + 1e-6)
+
+
+def test_geglu_fused_matches_unfused_halves():
+    g = synth.generator(600)
+    f, k, m = 384, 2048, 16
+    w = synth.weight(2 * f, k, g, "t4")
+    x = synth.activations(m, k, g).to(DEV)
+    q, s = w4.quantize_rowwise_int4(w.to(DEV))
+    fused = w4.w4a16_geglu_linear(x, q, s).double()
+    a = w4.w4a16_linear(x, q[:f].contiguous(), s[:f].contiguous()).double()
+    b = w4.w4a16_linear(x, q[f:].contiguous(), s[f:].contiguous()).double()
+    unfused = torch.nn.functional.gelu(a) * b
+    # the unfused path rounds a and b to fp16 first: allow for that
+    tol = 2 ** -10 * (a.abs() * 1.13 * b.abs() + a.abs() * b.abs()) + 2 ** -10 * unfused.abs() + 1e-3
+    assert torch.all((fused - unfused).abs() <= tol)
+
+
+# ----------------------------------------------------------- prefill GEMM
+
+@pytest.mark.parametrize("m,n,k", [(65, 300, 160), (128, 128, 128), (129, 257, 96),
+                                   (200, 1000, 1120), (256, 64, 32), (511, 33, 64)])
+def test_prefill_ragged_shapes(m, n, k):
+    g = synth.generator(m * 7 + n)
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill {m}x{n}x{k}")
+    check_linear(x, q, s, p_ref, s_ref, f"prefill {m}x{n}x{k}")
+    check_linear(x, q, s, p_ref, s_ref, f"prefill {m}x{n}x{k} bias", bias)
+
+
+@pytest.mark.parametrize("m", [65, 130, 300])
+def test_prefill_one_hot_and_pow2_bit_exact(m):
+    _one_hot_case(m, 300, 1024, 700 + m)
+    _pow2_case(m, 260, 1024, 800 + m)
+
+
+@pytest.mark.parametrize("m,f,k", [(65, 100, 256), (200, 300, 1024), (257, 64, 64)])
+def test_prefill_geglu_small(m, f, k):
+    g = synth.generator(900 + m)
+    w = synth.weight(2 * f, k, g, "t4")
+    x = synth.activations(m, k, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill geglu f={f}")
+    check_geglu(x, q, s, p_ref, s_ref, f"prefill geglu {m}x{f}x{k}")
+    bias = synth.normal_fp16((2 * f,), 0.5, g)
+    check_geglu(x, q, s, p_ref, s_ref, f"prefill geglu {m}x{f}x{k} bias", bias)
+
+
+# ------------------------------------------------------- misc properties
+
+def test_deterministic_reruns():
+    g = synth.generator(1000)
+    w = synth.weight(2048, 4096, g).to(DEV)
+    q, s = w4.quantize_rowwise_int4(w)
+    q2, s2 = w4.quantize_rowwise_int4(w)
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+    for m in (1, 32, 300):
+        x = synth.activations(m, 4096, g).to(DEV)
+        y1 = w4.w4a16_linear(x, q, s)
+        y2 = w4.w4a16_linear(x, q, s)
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), m
+
+
+def test_empty_and_rejected_calls():
+    x = torch.zeros(0, 64, dtype=torch.float16, device=DEV)
+    q = torch.zeros(16, 32, dtype=torch.uint8, device=DEV)
+    s = torch.zeros(16, dtype=torch.float16, device=DEV)
+    assert w4.w4a16_linear(x, q, s).shape == (0, 16)
+    assert w4.w4a16_geglu_linear(x, q, s).shape == (0, 8)
+    with pytest.raises(w4.W4A16Error):
+        w4.w4a16_linear(torch.zeros(2, 48, dtype=torch.float16, device=DEV),
+                        torch.zeros(4, 24, dtype=torch.uint8, device=DEV),
+                        torch.zeros(4, dtype=torch.float16, device=DEV))
+    with pytest.raises(w4.W4A16Error):
+        w4.quantize_rowwise_int4(torch.zeros(4, 3, dtype=torch.float16, device=DEV))

@@ -1,0 +1,132 @@
+"""MI355X (gfx950) weight-only INT4 row-wise quantization and W4A16 linears.
+
+GLM-130B's inference scheme (paper card on wikillm.com, "Method" and "Paper
+vs code"): each FP16 weight matrix [out][in] gets one absmax/7 scale per
+output row and integer codes in [-7, 7] packed two per byte; the linear layers
+keep FP16 activations.  This package is a thin binding over the C ABI of
+``include/w4a16.h`` (libw4a16.so, hand-written HIP kernels): it checks tensor
+placement, allocates outputs with torch, and passes raw device pointers and
+the current HIP stream.  Every step of the computation runs in the library.
+
+    q, s = quantize_rowwise_int4(w)            # w: cuda fp16 [n][k]
+    y = w4a16_linear(x, q, s, bias=None)       # x: cuda fp16 [m][k] -> [m][n]
+    g = w4a16_geglu_linear(x, q, s)            # q: [2f][k/2] -> [m][f]
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import W4A16Error
+
+__all__ = [
+    "quantize_rowwise_int4",
+    "w4a16_linear",
+    "w4a16_geglu_linear",
+    "W4A16Error",
+    "library",
+]
+
+
+def library():
+    """The loaded libw4a16.so (raises if it is not built)."""
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _require(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def quantize_rowwise_int4(w, q_out=None, s_out=None):
+    """W fp16 [n][k] (k even) -> (packed uint8 [n][k/2], scales fp16 [n])."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(w, torch.float16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [out_features][in_features]")
+    n, k = w.shape
+    if q_out is None:
+        q_out = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if s_out is None:
+        s_out = torch.empty((n,), dtype=torch.float16, device=w.device)
+    _require(q_out, torch.uint8, "q_out")
+    _require(s_out, torch.float16, "s_out")
+    if tuple(q_out.shape) != (n, k // 2) or tuple(s_out.shape) != (n,):
+        raise ValueError("output shape mismatch")
+    with torch.cuda.device(w.device):
+        st = lib.quantize_rowwise_int4(w.data_ptr(), n, k, q_out.data_ptr(), s_out.data_ptr(),
+                                       _stream_ptr(w.device))
+    _lib.check(st, "quantize_rowwise_int4")
+    return q_out, s_out
+
+
+def _linear_common(x, q, s, bias, out_cols, rows, y_out, name):
+    torch = _torch()
+    _require(x, torch.float16, "x")
+    _require(q, torch.uint8, "q")
+    _require(s, torch.float16, "s")
+    if x.dim() != 2 or q.dim() != 2 or s.dim() != 1:
+        raise ValueError(f"{name}: x [m][k], q [rows][k/2], s [rows] expected")
+    m, k = x.shape
+    if q.shape[0] != rows or q.shape[1] * 2 != k or s.shape[0] != rows:
+        raise ValueError(f"{name}: shape mismatch x {tuple(x.shape)} q {tuple(q.shape)} s {tuple(s.shape)}")
+    for t, nm in ((q, "q"), (s, "s")):
+        if t.device != x.device:
+            raise ValueError(f"{name}: {nm} on {t.device}, x on {x.device}")
+    if bias is not None:
+        _require(bias, torch.float16, "bias")
+        if tuple(bias.shape) != (rows,) or bias.device != x.device:
+            raise ValueError(f"{name}: bias must be fp16 [{rows}] on {x.device}")
+    if y_out is None:
+        y_out = torch.empty((m, out_cols), dtype=torch.float16, device=x.device)
+    _require(y_out, torch.float16, "y_out")
+    if tuple(y_out.shape) != (m, out_cols):
+        raise ValueError(f"{name}: y_out must be [{m}][{out_cols}]")
+    return m, k, y_out
+
+
+def w4a16_linear(x, q, s, bias=None, y_out=None):
+    """y[m][n] = fp16(s * (x . q^T) + bias): fp16 activations, INT4 weights."""
+    lib = _lib.load()
+    n = q.shape[0]
+    m, k, y_out = _linear_common(x, q, s, bias, n, n, y_out, "w4a16_linear")
+    torch = _torch()
+    with torch.cuda.device(x.device):
+        st = lib.w4a16_linear(x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), n,
+                              None if bias is None else bias.data_ptr(), y_out.data_ptr(),
+                              _stream_ptr(x.device))
+    _lib.check(st, "w4a16_linear")
+    return y_out
+
+
+def w4a16_geglu_linear(x, q, s, bias=None, y_out=None):
+    """y[m][f] = fp16(GELU(a) * b), a / b the linears through rows [0,f) / [f,2f)."""
+    lib = _lib.load()
+    rows = q.shape[0]
+    if rows % 2:
+        raise ValueError("w4a16_geglu_linear: q must have an even number of rows (2f)")
+    f = rows // 2
+    m, k, y_out = _linear_common(x, q, s, bias, f, rows, y_out, "w4a16_geglu_linear")
+    torch = _torch()
+    with torch.cuda.device(x.device):
+        st = lib.w4a16_geglu_linear(x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), f,
+                                    None if bias is None else bias.data_ptr(), y_out.data_ptr(),
+                                    _stream_ptr(x.device))
+    _lib.check(st, "w4a16_geglu_linear")
+    return y_out

@@ -1,0 +1,154 @@
+// C ABI of the W4A16 library: argument checks, kernel selection, error
+// mapping.  Contract and citations: include/w4a16.h.
+#include "../../include/w4a16.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+namespace w4a16 {
+hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
+                           hipStream_t stream);
+hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
+                         int64_t n_out, const void *bias, void *y, bool geglu, hipStream_t stream);
+hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
+                          const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
+                          hipStream_t stream);
+}  // namespace w4a16
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+// Largest dimension accepted: grids and in-kernel int arithmetic stay far
+// from overflow, and the largest GLM-130B shapes (65536 rows, 32768 columns,
+// 2048 tokens) fit with room to spare.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kDecodeMaxM = 64;
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+w4a16_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) {
+        g_last_error[0] = '\0';
+        return W4A16_OK;
+    }
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction)
+        return W4A16_ERR_DEVICE;
+    return W4A16_ERR_HIP;
+}
+
+// Sizes first: an empty call (m == 0 or rows == 0) is valid whatever the
+// pointers are (torch hands out NULL for empty tensors).
+w4a16_status check_gemm_shape(int64_t m, int64_t k, int64_t rows)
+{
+    if (m < 0 || rows < 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || rows > kMaxDim ||
+        k > kMaxDim || m * k > (int64_t(1) << 40) || m * rows > (int64_t(1) << 40))
+        return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const void *bias,
+                             const void *y)
+{
+    if (!x || !q || !s || !y)
+        return W4A16_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(y) ||
+        (bias && !aligned16(bias)))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, const void *s,
+                        int64_t n_out, const void *bias, void *y, bool geglu, void *stream)
+{
+    const int64_t rows = geglu ? 2 * n_out : n_out;
+    w4a16_status st = check_gemm_shape(m, k, rows);
+    if (st != W4A16_OK)
+        return st;
+    if (m == 0 || n_out == 0)
+        return W4A16_OK;
+    st = check_gemm_ptrs(x, q, s, bias, y);
+    if (st != W4A16_OK)
+        return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (m <= kDecodeMaxM)
+        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, hs);
+    else
+        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, hs);
+    return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status quantize_rowwise_int4(const void *w_fp16, int64_t n, int64_t k, void *q_packed,
+                                   void *scales_fp16, void *stream)
+{
+    if (n < 0 || k < 2 || k % 2 != 0 || n > 0x7FFFFFFF || k > kMaxDim)
+        return W4A16_ERR_SHAPE;
+    if (n == 0)
+        return W4A16_OK;
+    if (!w_fp16 || !q_packed || !scales_fp16)
+        return W4A16_ERR_NULL;
+    if (!aligned16(w_fp16) || !aligned16(q_packed) || !aligned16(scales_fp16))
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_quantize(w_fp16, n, k, q_packed, scales_fp16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k, const void *q_packed,
+                          const void *scales_fp16, int64_t n, const void *bias_fp16, void *y_fp16,
+                          void *stream)
+{
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, stream);
+}
+
+w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const void *q_packed,
+                                const void *scales_fp16, int64_t f, const void *bias_fp16,
+                                void *y_fp16, void *stream)
+{
+    if (f > kMaxDim / 2)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, stream);
+}
+
+const char *w4a16_status_string(int status)
+{
+    switch (status) {
+    case W4A16_OK:
+        return "ok";
+    case W4A16_ERR_NULL:
+        return "a required pointer is NULL";
+    case W4A16_ERR_SHAPE:
+        return "invalid shape (negative size, k = 0, k not even for quantize, k % 32 != 0 for the "
+               "linears, or size too large)";
+    case W4A16_ERR_ALIGN:
+        return "a pointer is not 16-byte aligned";
+    case W4A16_ERR_HIP:
+        return "HIP runtime error";
+    case W4A16_ERR_DEVICE:
+        return "no gfx950 code for the current device";
+    default:
+        return "unknown status";
+    }
+}
+
+const char *w4a16_last_error(void)
+{
+    return g_last_error;
+}
+
+int w4a16_abi_version(void)
+{
+    return W4A16_ABI_VERSION;
+}
+
+}  // extern "C"

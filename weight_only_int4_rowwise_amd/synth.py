@@ -73,41 +73,43 @@ def activations(m: int, k: int, gen: torch.Generator, device: str = "cpu") -> to
 
 
 # ---------------------------------------------------------------------------
-# Workloads (each returns CPU fp16 tensors; the caller moves them)
+# Workloads.  Tensors are drawn on `device` with a generator of that device
+# (the CPU and GPU generators give different streams for the same seed; both
+# sides of a comparison always receive the very same tensors).
 # ---------------------------------------------------------------------------
 
-def toy(seed: int = 0):
+def toy(seed: int = 0, device: str = "cpu"):
     """Weight 1024 x 1024 ~ N(0, 0.02^2); activations for M = 1 and M = 16."""
-    g = generator(seed)
-    w = weight(1024, 1024, g)
-    x1 = activations(1, 1024, g)
-    x16 = activations(16, 1024, g)
+    g = generator(seed, device)
+    w = weight(1024, 1024, g, device=device)
+    x1 = activations(1, 1024, g, device)
+    x16 = activations(16, 1024, g, device)
     return w, {1: x1, 16: x16}
 
 
-def qkv_decode(ms=(1, 8, 32, 64), seed: int = 0):
+def qkv_decode(ms=(1, 8, 32, 64), seed: int = 0, device: str = "cpu"):
     """QKV projection 36864 x 12288 ~ N(0, 0.02^2); activations per M."""
-    g = generator(seed)
-    w = weight(QKV_OUT, HIDDEN, g)
-    return w, {m: activations(m, HIDDEN, g) for m in ms}
+    g = generator(seed, device)
+    w = weight(QKV_OUT, HIDDEN, g, device=device)
+    return w, {m: activations(m, HIDDEN, g, device) for m in ms}
 
 
-def geglu_decode(ms=(1, 16), seed: int = 0):
+def geglu_decode(ms=(1, 16), seed: int = 0, device: str = "cpu"):
     """GeGLU up 65536 x 12288 and down 12288 x 32768, t(4) * 0.02 weights."""
-    g = generator(seed)
-    w_up = weight(2 * FFN, HIDDEN, g, "t4")
-    w_down = weight(HIDDEN, FFN, g, "t4")
-    x_up = {m: activations(m, HIDDEN, g) for m in ms}
-    x_down = {m: activations(m, FFN, g) for m in ms}
+    g = generator(seed, device)
+    w_up = weight(2 * FFN, HIDDEN, g, "t4", device)
+    w_down = weight(HIDDEN, FFN, g, "t4", device)
+    x_up = {m: activations(m, HIDDEN, g, device) for m in ms}
+    x_down = {m: activations(m, FFN, g, device) for m in ms}
     return w_up, w_down, x_up, x_down
 
 
-def prefill(seed: int = 0, m: int = SEQ):
+def prefill(seed: int = 0, m: int = SEQ, device: str = "cpu"):
     """Attention-out 12288 x 12288 and FFN-up 65536 x 12288 ~ N(0, 0.02^2); M = 2048."""
-    g = generator(seed)
-    w_attn = weight(HIDDEN, HIDDEN, g)
-    w_up = weight(2 * FFN, HIDDEN, g)
-    x = activations(m, HIDDEN, g)
+    g = generator(seed, device)
+    w_attn = weight(HIDDEN, HIDDEN, g, device=device)
+    w_up = weight(2 * FFN, HIDDEN, g, device=device)
+    x = activations(m, HIDDEN, g, device)
     return w_attn, w_up, x
 
 
@@ -127,21 +129,15 @@ def all_finite_nonneg_fp16() -> torch.Tensor:
 
 def enumeration_rows(absmax_bits, k: int) -> torch.Tensor:
     """One row per absmax bit pattern a: the row holds +a, then every fp16
-    value v with 0 < |v| <= a in both signs, in increasing bit order, repeated
-    cyclically to fill k entries.  Every (absmax, weight) pair that can occur
-    in a row with that absmax appears once per row if k is large enough."""
-    rows = []
-    for a in absmax_bits:
-        a = int(a)
-        pos = torch.arange(1, a + 1, dtype=torch.int32)
-        vals = torch.cat([pos, pos | 0x8000]) if a > 0 else torch.zeros(0, dtype=torch.int32)
-        body = torch.cat([torch.tensor([a], dtype=torch.int32), vals])
-        reps = -(-k // body.numel())
-        row = body.repeat(reps)[:k]
-        rows.append(row)
-    bits = torch.stack(rows).to(torch.int32)
-    bits = torch.where(bits >= 0x8000, bits - 0x10000, bits).to(torch.int16)
-    return bits.view(torch.float16)
+    value v with 0 < |v| <= a (positive bit patterns 1..a, then the same with
+    the sign bit), repeated cyclically to fill k entries.  With k >= 2a + 1
+    every weight that can occur in a row with absmax a appears in it."""
+    a = torch.as_tensor(absmax_bits, dtype=torch.int64).reshape(-1, 1)
+    j = torch.arange(k, dtype=torch.int64).reshape(1, -1)
+    idx = j % (2 * a + 1)
+    val = torch.where(idx == 0, a, torch.where(idx <= a, idx, (idx - a) | 0x8000))
+    val = torch.where(val >= 0x8000, val - 0x10000, val)
+    return val.to(torch.int16).view(torch.float16)
 
 
 def exponent_rows(n: int, k: int, gen: torch.Generator, e_lo: int = -8, e_hi: int = 0) -> torch.Tensor:
