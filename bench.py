@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X W4A16 row-wise INT4 path at GLM-130B shapes.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+
+Headline workload: the GLM-130B decode QKV projection, weight 36864 x 12288
+quantized INT4 row-wise (N(0, 0.02^2) weights), fp16 activations
+M in {1, 8, 32, 64}.  One step = one w4a16_linear launch per M (the memory-
+bound decode kernel).  The weights rotate over 5 independently drawn
+matrices (1.13 GB of packed weights, over 4x the 256 MB last-level cache),
+so every launch streams its weights from HBM.  `value` is the algorithmic
+bytes of the step (packed weights + scales + activations + outputs) over
+its time: HBM GB/s.
+
+The same JSON line also carries, measured in the same run:
+  roofline      the dominant decode launch against 8 TB/s HBM
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  extra         GeGLU decode (fused up-projection, down-projection),
+                prefill GEMM TFLOP/s (attention-out and fused FFN-up at
+                M = 2048) against the 2.5 PFLOP/s fp16 MFMA peak, the
+                quantizer, and the full 70-layer decode step at M = 8.
+Inputs are synthetic, seeded and resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_F16_PEAK_TFS = 2516.6     # MI355X dense fp16 MFMA, 2.5 PFLOP/s
+METRIC = "W4A16 linear: decode HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak)"
+DECODE_MS = (1, 8, 32, 64)
+ROTATE = 5
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def linear_bytes(m, n_rows, k, n_out):
+    """Algorithmic bytes of one W4A16 linear: packed weights, fp16 scales,
+    fp16 activations in, fp16 outputs out."""
+    return n_rows * k // 2 + 2 * n_rows + 2 * m * k + 2 * m * n_out
+
+
+def csrc_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "weight_only_int4_rowwise_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(torch, fn, reps, warm=2):
+    """Average duration (s) of fn() over reps back-to-back launches, timed
+    with events on the current stream (the stream the kernels run on)."""
+    for _ in range(warm):
+        fn()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def make_rotating(torch, w4, synth, n, k, dist, count, seed0, dev):
+    qs = []
+    for i in range(count):
+        g = synth.generator(seed0 + i, dev)
+        w = synth.weight(n, k, g, dist, dev)
+        q, s = w4.quantize_rowwise_int4(w)
+        del w
+        qs.append((q, s))
+    torch.cuda.synchronize()
+    return qs
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
+    ap.add_argument("--no-full-step", action="store_true", help="skip the 70-layer decode step")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import weight_only_int4_rowwise_amd as w4
+    from weight_only_int4_rowwise_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    w4.library()      # raises if the HIP library is not built
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    N, K = synth.QKV_OUT, synth.HIDDEN
+
+    # ------------------------------------------------------------ headline
+    log(f"preparing {ROTATE} QKV weights {N}x{K} on the GPU")
+    qkv = make_rotating(torch, w4, synth, N, K, "normal", ROTATE, 10, dev)
+    gx = synth.generator(0, dev)
+    xs = {m: synth.activations(m, K, gx, dev) for m in DECODE_MS}
+    ys = {m: torch.empty(m, N, dtype=torch.float16, device=dev) for m in DECODE_MS}
+    step_bytes = sum(linear_bytes(m, N, K, N) for m in DECODE_MS)
+
+    it = [0]
+
+    def step():
+        for m in DECODE_MS:
+            q, s = qkv[it[0] % ROTATE]
+            it[0] += 1
+            w4.w4a16_linear(xs[m], q, s, y_out=ys[m])
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(a.steps):
+        step()
+    t1.record()
+    t1.synchronize()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    log(f"headline: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+
+    # per-M launch durations (roofline of the dominant decode launch)
+    per_m = {}
+    for m in DECODE_MS:
+        j = [0]
+
+        def one(m=m, j=j):
+            q, s = qkv[j[0] % ROTATE]
+            j[0] += 1
+            w4.w4a16_linear(xs[m], q, s, y_out=ys[m])
+
+        t = time_launches(torch, one, 40)
+        b = linear_bytes(m, N, K, N)
+        per_m[m] = {"us": round(t * 1e6, 2), "bytes": b, "GBs": round(b / t / 1e9, 1),
+                    "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "mfma_frac_needed": round(2.0 * m * N * K / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+        log(f"decode QKV M={m}: {t * 1e6:.1f} us, {b / t / 1e9:.0f} GB/s")
+    dom = max(DECODE_MS, key=lambda m: per_m[m]["us"])
+    mb = (dom + 15) // 16
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "decode_qkv_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        if tr.get("csrc_hash") == csrc_hash() and str(dom) in tr.get("bytes_per_launch", {}):
+            traffic = tr["bytes_per_launch"][str(dom)]
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"decode_kernel (M={dom}, {mb} token block{'s' if mb > 1 else ''}), QKV 36864x12288",
+        "achieved": per_m[dom]["GBs"],
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(per_m[dom]["GBs"] / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": per_m[dom]["bytes"],
+        "avg_launch_us": per_m[dom]["us"],
+    }
+
+    # ------------------------------------------------------- cpu baseline
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        rows = 2048
+        q0, s0 = qkv[0]
+        p_host = q0[:rows].cpu().numpy()
+        s_host = s0[:rows].cpu().view(torch.int16).numpy().view("uint16")
+        tot_b, tot_t = 0, 0.0
+        for m in DECODE_MS:
+            xh = xs[m].cpu().view(torch.int16).numpy().view("uint16")
+            c0 = time.perf_counter()
+            oracle.linear(xh, p_host, s_host)
+            tot_t += time.perf_counter() - c0
+            tot_b += linear_bytes(m, rows, K, rows)
+        cpu = {"value": round(tot_b / tot_t / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"oracle.linear (fp64, plain loops, OpenMP over outputs) on the first {rows} of "
+                         f"{N} QKV rows at M = 1, 8, 32, 64 ({tot_t:.1f} s of CPU time); "
+                         "same algorithmic-byte accounting as value"}
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    # -------------------------------------------------------------- extra
+    extra = {"decode_qkv_per_m": {str(m): v for m, v in per_m.items()}}
+    del ys
+    if not a.no_extra:
+        extra.update(extra_workloads(torch, w4, synth, dev, a))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "GLM-130B decode QKV projection: INT4 row-wise weight 36864x12288 "
+                        "(N(0,0.02^2)), fp16 activations M in {1,8,32,64}, one launch per M per step",
+            "N": N, "K": K, "M": list(DECODE_MS),
+            "rotating_weight_buffers": ROTATE,
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def extra_workloads(torch, w4, synth, dev, a):
+    res = {}
+    H, F = synth.HIDDEN, synth.FFN
+
+    # GeGLU decode: fused up-projection 65536 x 12288 and down 12288 x 32768, t(4) weights
+    log("GeGLU decode")
+    ups = make_rotating(torch, w4, synth, 2 * F, H, "t4", 3, 100, dev)
+    downs = make_rotating(torch, w4, synth, H, F, "t4", 5, 200, dev)
+    g = synth.generator(1, dev)
+    gd = {}
+    for m in (1, 16):
+        xu = synth.activations(m, H, g, dev)
+        xd = synth.activations(m, F, g, dev)
+        yu = torch.empty(m, F, dtype=torch.float16, device=dev)
+        yd = torch.empty(m, H, dtype=torch.float16, device=dev)
+        c = [0]
+
+        def up(c=c, xu=xu, yu=yu):
+            q, s = ups[c[0] % len(ups)]
+            c[0] += 1
+            w4.w4a16_geglu_linear(xu, q, s, y_out=yu)
+
+        def down(c=c, xd=xd, yd=yd):
+            q, s = downs[c[0] % len(downs)]
+            c[0] += 1
+            w4.w4a16_linear(xd, q, s, y_out=yd)
+
+        tu = time_launches(torch, up, 30)
+        td = time_launches(torch, down, 30)
+        bu = linear_bytes(m, 2 * F, H, F)
+        bd = linear_bytes(m, H, F, H)
+        gd[str(m)] = {"up_geglu_us": round(tu * 1e6, 2), "up_geglu_GBs": round(bu / tu / 1e9, 1),
+                      "down_us": round(td * 1e6, 2), "down_GBs": round(bd / td / 1e9, 1)}
+        log(f"GeGLU decode M={m}: up {bu / tu / 1e9:.0f} GB/s, down {bd / td / 1e9:.0f} GB/s")
+    res["decode_geglu_ffn"] = gd
+    del downs
+
+    # prefill: attention-out 12288 x 12288 and FFN-up 65536 x 12288 at M = 2048
+    log("prefill")
+    M = synth.SEQ
+    attn = make_rotating(torch, w4, synth, H, H, "normal", 2, 300, dev)
+    x = synth.activations(M, H, g, dev)
+    pf = {}
+    y1 = torch.empty(M, H, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.w4a16_linear(x, attn[0][0], attn[0][1], y_out=y1), 10)
+    fl = 2.0 * M * H * H
+    pf["attn_out"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                      "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    del y1
+    y2 = torch.empty(M, F, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.w4a16_geglu_linear(x, ups[0][0], ups[0][1], y_out=y2), 5)
+    fl = 2.0 * M * 2 * F * H
+    pf["ffn_up_geglu"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                          "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    del y2
+    y3 = torch.empty(M, 2 * F, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.w4a16_linear(x, ups[0][0], ups[0][1], y_out=y3), 5)
+    pf["ffn_up_plain"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                          "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    del y3
+    # the fp16 GEMM of the same shape through torch, as a context ceiling
+    wf = synth.weight(H, H, g, device=dev)
+    yt = torch.empty(M, H, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: torch.matmul(x, wf.t(), out=yt), 10)
+    pf["context_torch_fp16_matmul_attn_out"] = {"us": round(t * 1e6, 1),
+                                                "TFLOPs": round(2.0 * M * H * H / t / 1e12, 1)}
+    del wf, yt
+    res["prefill_m2048"] = pf
+    log(f"prefill: {pf}")
+    del ups, attn
+
+    # quantizer: QKV-shaped fp16 weight -> packed + scales
+    log("quantizer")
+    wq = synth.weight(synth.QKV_OUT, H, g, device=dev)
+    qo = torch.empty(synth.QKV_OUT, H // 2, dtype=torch.uint8, device=dev)
+    so = torch.empty(synth.QKV_OUT, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.quantize_rowwise_int4(wq, q_out=qo, s_out=so), 10)
+    qb = synth.QKV_OUT * H * 2 + synth.QKV_OUT * H // 2 + 2 * synth.QKV_OUT
+    res["quantize_qkv"] = {"us": round(t * 1e6, 1), "GBs": round(qb / t / 1e9, 1),
+                           "frac_hbm": round(qb / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del wq, qo, so
+
+    if not a.no_full_step:
+        res["full_decode_step_m8"] = full_step(torch, w4, synth, dev)
+    return res
+
+
+def full_step(torch, w4, synth, dev):
+    """70 layers x (QKV, attention-out, fused GeGLU up, down) at M = 8, all
+    weights resident (63.4 GB packed), launched back to back on one stream."""
+    log("full 70-layer decode step: generating and quantizing 280 matrices")
+    H, F = synth.HIDDEN, synth.FFN
+    layers = []
+    for l in range(synth.LAYERS):
+        mats = []
+        for mid, (name, n, k) in enumerate(synth.LAYER_LINEARS):
+            g = synth.generator(synth.layer_weight_seed(l, mid), dev)
+            w = synth.weight(n, k, g, device=dev)
+            mats.append(w4.quantize_rowwise_int4(w))
+            del w
+        layers.append(mats)
+    torch.cuda.synchronize()
+    g = synth.generator(7, dev)
+    M = 8
+    xh = synth.activations(M, H, g, dev)
+    xf = synth.activations(M, F, g, dev)
+    y_qkv = torch.empty(M, synth.QKV_OUT, dtype=torch.float16, device=dev)
+    y_h = torch.empty(M, H, dtype=torch.float16, device=dev)
+    y_f = torch.empty(M, F, dtype=torch.float16, device=dev)
+
+    def run():
+        for mats in layers:
+            w4.w4a16_linear(xh, mats[0][0], mats[0][1], y_out=y_qkv)
+            w4.w4a16_linear(xh, mats[1][0], mats[1][1], y_out=y_h)
+            w4.w4a16_geglu_linear(xh, mats[2][0], mats[2][1], y_out=y_f)
+            w4.w4a16_linear(xf, mats[3][0], mats[3][1], y_out=y_h)
+
+    t = time_launches(torch, run, 3, warm=1)
+    total = 0
+    for name, n, k in synth.LAYER_LINEARS:
+        out = n // 2 if name == "ffn_up" else n
+        total += linear_bytes(M, n, k, out)
+    total *= synth.LAYERS
+    r = {"ms": round(t * 1e3, 3), "bytes": total, "GBs": round(total / t / 1e9, 1),
+         "frac_hbm": round(total / t / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"full step: {r}")
+    del layers
+    torch.cuda.empty_cache()
+    return r
+
+
+if __name__ == "__main__":
+    sys.exit(main())
