@@ -122,6 +122,44 @@ w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k,
                                 const void *q_packed, const void *scales_fp16, int64_t f,
                                 const void *bias_fp16, void *y_fp16, void *stream);
 
+/*
+ * Prepacked layout -- the load-time weight layout transform that the
+ * pages' FasterTransformer port applies ("pre-transposing parameters",
+ * paperlayer.ai summary, section B.5), here for gfx950's matrix cores.
+ *
+ * Same packed bytes and nibble encoding as quantize_rowwise_int4's output,
+ * in another order: the weight is cut into tiles of 16 rows x 128 input
+ * features (1024 bytes); tile (g, t) -- rows [16g, 16g+16), features
+ * [128t, 128t+128) -- is stored at byte ((g * ceil(k/128)) + t) * 1024, and
+ * inside it the 16 bytes at offset 16 * l (l = 16 j + r, j < 4, r < 16) are
+ * packed bytes [64t + 16j, 64t + 16j + 16) of row 16g + r.  Rows past n and
+ * features past k are zero codes.  Each tile is then one contiguous read
+ * in exactly the order the kernels consume it.
+ *
+ * w4a16_prepacked_bytes: size of the prepacked buffer,
+ *   ceil(n/16) * ceil(k/128) * 1024, or -1 if n < 0, k <= 0 or k % 32 != 0.
+ * w4a16_prepack: q_packed [n][k/2] (device) -> q_prepacked (device,
+ *   w4a16_prepacked_bytes(n, k) bytes).  k % 32 == 0.
+ * w4a16_linear_prepacked / w4a16_geglu_linear_prepacked: exactly
+ *   w4a16_linear / w4a16_geglu_linear with the weight in the prepacked
+ *   layout; the GeGLU form needs f % 16 == 0 (the gate / value boundary
+ *   falls on a tile boundary).  Results are bit-identical to the row-major
+ *   calls for the same m (same kernels, same summation order).
+ */
+int64_t w4a16_prepacked_bytes(int64_t n, int64_t k);
+
+w4a16_status w4a16_prepack(const void *q_packed, int64_t n, int64_t k, void *q_prepacked,
+                           void *stream);
+
+w4a16_status w4a16_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                    const void *q_prepacked, const void *scales_fp16, int64_t n,
+                                    const void *bias_fp16, void *y_fp16, void *stream);
+
+w4a16_status w4a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                          const void *q_prepacked, const void *scales_fp16,
+                                          int64_t f, const void *bias_fp16, void *y_fp16,
+                                          void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *w4a16_status_string(int status);
 

@@ -95,3 +95,26 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(4, 32, dtype=torch.float16)
     with pytest.raises(ValueError, match="no CPU path"):
         w4.quantize_rowwise_int4(w)
+
+
+def test_prepacked_size_and_checks(lib):
+    assert lib.w4a16_prepacked_bytes(16, 128) == 1024
+    assert lib.w4a16_prepacked_bytes(17, 128) == 2048
+    assert lib.w4a16_prepacked_bytes(16, 160) == 2048
+    assert lib.w4a16_prepacked_bytes(36864, 12288) == 36864 * 12288 // 2
+    assert lib.w4a16_prepacked_bytes(0, 64) == 0
+    assert lib.w4a16_prepacked_bytes(-1, 64) == -1
+    assert lib.w4a16_prepacked_bytes(16, 48) == -1
+    assert lib.w4a16_prepacked_bytes(16, 0) == -1
+    p = lib.w4a16_prepack
+    assert p(None, 16, 64, B, None) == _lib.ERR_NULL
+    assert p(A, 16, 64, None, None) == _lib.ERR_NULL
+    assert p(A, 16, 48, B, None) == _lib.ERR_SHAPE
+    assert p(MIS, 16, 64, B, None) == _lib.ERR_ALIGN
+    assert p(None, 0, 64, None, None) == _lib.OK
+    g = lib.w4a16_geglu_linear_prepacked
+    assert g(A, 1, 64, B, C, 24, None, D, None) == _lib.ERR_SHAPE     # f % 16 != 0
+    assert g(A, 1, 64, B, C, 32, None, MIS, None) == _lib.ERR_ALIGN
+    lp = lib.w4a16_linear_prepacked
+    assert lp(A, 1, 48, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+    assert lp(None, 1, 64, B, C, 16, None, D, None) == _lib.ERR_NULL

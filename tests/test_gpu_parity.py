@@ -271,3 +271,65 @@ def test_empty_and_rejected_calls():
                         torch.zeros(4, dtype=torch.float16, device=DEV))
     with pytest.raises(w4.W4A16Error):
         w4.quantize_rowwise_int4(torch.zeros(4, 3, dtype=torch.float16, device=DEV))
+
+
+# ------------------------------------------------------------ prepacked layout
+
+def _prepack_reference(p_ref: np.ndarray, n: int, k: int) -> np.ndarray:
+    """The prepacked layout written out from its definition (include/w4a16.h)."""
+    ng, kt = -(-n // 16), -(-k // 128)
+    out = np.zeros((ng, kt, 64, 16), dtype=np.uint8)
+    padded = np.zeros((ng * 16, kt * 64), dtype=np.uint8)
+    padded[:n, :k // 2] = p_ref
+    for lane in range(64):
+        r, j = lane % 16, lane // 16
+        for t in range(kt):
+            out[:, t, lane, :] = padded[r::16, 64 * t + 16 * j: 64 * t + 16 * j + 16]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(48, 256), (37, 160), (1000, 1120), (16, 128)])
+def test_prepack_layout_matches_definition(n, k):
+    g = synth.generator(1100 + n)
+    w = synth.weight(n, k, g, "t4")
+    q, s, p_ref, s_ref = quantize_both(w, f"prepack {n}x{k}")
+    announce("prepack", n, k)
+    qp = w4.w4a16_prepack(q)
+    torch.cuda.synchronize()
+    assert qp.numel() == w4.w4a16_prepacked_bytes(n, k)
+    assert_bits_equal(u8(qp), _prepack_reference(p_ref, n, k), f"prepack {n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 33, 64, 65, 130, 300])
+def test_prepacked_linear_bit_identical_to_row_major(m):
+    g = synth.generator(1200 + m)
+    n, k = 1000, 1120
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g).to(DEV)
+    bias = synth.normal_fp16((n,), 0.5, g).to(DEV)
+    q, s = w4.quantize_rowwise_int4(w.to(DEV))
+    qp = w4.w4a16_prepack(q)
+    announce("prepacked linear", m, n, k)
+    for b in (None, bias):
+        y0 = w4.w4a16_linear(x, q, s, b)
+        y1 = w4.w4a16_linear_prepacked(x, qp, s, b)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(y1), bits(y0), f"prepacked vs row-major m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 40, 64, 130])
+def test_prepacked_geglu_bit_identical_to_row_major(m):
+    g = synth.generator(1300 + m)
+    f, k = 512, 1056
+    w = synth.weight(2 * f, k, g, "t4")
+    x = synth.activations(m, k, g).to(DEV)
+    q, s = w4.quantize_rowwise_int4(w.to(DEV))
+    qp = w4.w4a16_prepack(q)
+    announce("prepacked geglu", m, f, k)
+    y0 = w4.w4a16_geglu_linear(x, q, s)
+    y1 = w4.w4a16_geglu_linear_prepacked(x, qp, s)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(y1), bits(y0), f"prepacked geglu m={m}")
+    with pytest.raises(w4.W4A16Error):
+        q2, s2 = w4.quantize_rowwise_int4(synth.weight(2 * 24, k, g).to(DEV))
+        w4.w4a16_geglu_linear_prepacked(x, w4.w4a16_prepack(q2), s2)

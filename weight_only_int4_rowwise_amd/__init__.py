@@ -11,6 +11,9 @@ the current HIP stream.  Every step of the computation runs in the library.
     q, s = quantize_rowwise_int4(w)            # w: cuda fp16 [n][k]
     y = w4a16_linear(x, q, s, bias=None)       # x: cuda fp16 [m][k] -> [m][n]
     g = w4a16_geglu_linear(x, q, s)            # q: [2f][k/2] -> [m][f]
+
+    qp = w4a16_prepack(q)                      # load-time tile layout, same bytes
+    y = w4a16_linear_prepacked(x, qp, s)       # identical results, faster reads
 """
 from __future__ import annotations
 
@@ -21,6 +24,10 @@ __all__ = [
     "quantize_rowwise_int4",
     "w4a16_linear",
     "w4a16_geglu_linear",
+    "w4a16_prepacked_bytes",
+    "w4a16_prepack",
+    "w4a16_linear_prepacked",
+    "w4a16_geglu_linear_prepacked",
     "W4A16Error",
     "library",
 ]
@@ -129,4 +136,88 @@ def w4a16_geglu_linear(x, q, s, bias=None, y_out=None):
                                     None if bias is None else bias.data_ptr(), y_out.data_ptr(),
                                     _stream_ptr(x.device))
     _lib.check(st, "w4a16_geglu_linear")
+    return y_out
+
+
+def w4a16_prepacked_bytes(n: int, k: int) -> int:
+    """Bytes of the prepacked layout of an [n][k] weight (-1 for bad sizes)."""
+    return int(_lib.load().w4a16_prepacked_bytes(int(n), int(k)))
+
+
+def w4a16_prepack(q, q_out=None):
+    """Row-major packed codes [n][k/2] -> prepacked tile layout (uint8, 1-D)."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(q, torch.uint8, "q")
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D [n][k/2]")
+    n, k = q.shape[0], 2 * q.shape[1]
+    size = lib.w4a16_prepacked_bytes(n, k)
+    if size < 0:
+        raise ValueError(f"w4a16_prepack: bad shape n={n} k={k} (k % 32 must be 0)")
+    if q_out is None:
+        q_out = torch.empty((size,), dtype=torch.uint8, device=q.device)
+    _require(q_out, torch.uint8, "q_out")
+    if q_out.numel() != size or q_out.device != q.device:
+        raise ValueError(f"w4a16_prepack: q_out must hold {size} bytes on {q.device}")
+    with torch.cuda.device(q.device):
+        st = lib.w4a16_prepack(q.data_ptr(), n, k, q_out.data_ptr(), _stream_ptr(q.device))
+    _lib.check(st, "w4a16_prepack")
+    return q_out
+
+
+def _prepacked_common(x, qp, s, bias, out_cols, rows, y_out, name):
+    torch = _torch()
+    lib = _lib.load()
+    _require(x, torch.float16, "x")
+    _require(qp, torch.uint8, "qp")
+    _require(s, torch.float16, "s")
+    if x.dim() != 2 or s.dim() != 1 or s.shape[0] != rows:
+        raise ValueError(f"{name}: x [m][k] and s [{rows}] expected")
+    m, k = x.shape
+    size = lib.w4a16_prepacked_bytes(rows, k)
+    if size < 0 or qp.numel() != size:
+        raise ValueError(f"{name}: prepacked weight must hold {size} bytes for {rows} x {k}")
+    for t, nm in ((qp, "qp"), (s, "s")):
+        if t.device != x.device:
+            raise ValueError(f"{name}: {nm} on {t.device}, x on {x.device}")
+    if bias is not None:
+        _require(bias, torch.float16, "bias")
+        if tuple(bias.shape) != (rows,) or bias.device != x.device:
+            raise ValueError(f"{name}: bias must be fp16 [{rows}] on {x.device}")
+    if y_out is None:
+        y_out = torch.empty((m, out_cols), dtype=torch.float16, device=x.device)
+    _require(y_out, torch.float16, "y_out")
+    if tuple(y_out.shape) != (m, out_cols):
+        raise ValueError(f"{name}: y_out must be [{m}][{out_cols}]")
+    return lib, m, k, y_out
+
+
+def w4a16_linear_prepacked(x, qp, s, bias=None, y_out=None):
+    """w4a16_linear with the weight in the prepacked layout (n = len(s))."""
+    torch = _torch()
+    n = s.shape[0]
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, n, n, y_out, "w4a16_linear_prepacked")
+    with torch.cuda.device(x.device):
+        st = lib.w4a16_linear_prepacked(x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), n,
+                                        None if bias is None else bias.data_ptr(),
+                                        y_out.data_ptr(), _stream_ptr(x.device))
+    _lib.check(st, "w4a16_linear_prepacked")
+    return y_out
+
+
+def w4a16_geglu_linear_prepacked(x, qp, s, bias=None, y_out=None):
+    """w4a16_geglu_linear with the weight in the prepacked layout (f = len(s) / 2)."""
+    torch = _torch()
+    rows = s.shape[0]
+    if rows % 2:
+        raise ValueError("w4a16_geglu_linear_prepacked: s must have 2f entries")
+    f = rows // 2
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, f, rows, y_out,
+                                         "w4a16_geglu_linear_prepacked")
+    with torch.cuda.device(x.device):
+        st = lib.w4a16_geglu_linear_prepacked(x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
+                                              None if bias is None else bias.data_ptr(),
+                                              y_out.data_ptr(), _stream_ptr(x.device))
+    _lib.check(st, "w4a16_geglu_linear_prepacked")
     return y_out

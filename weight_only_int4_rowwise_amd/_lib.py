@@ -19,6 +19,10 @@ EXPORTS = (
     "quantize_rowwise_int4",
     "w4a16_linear",
     "w4a16_geglu_linear",
+    "w4a16_prepacked_bytes",
+    "w4a16_prepack",
+    "w4a16_linear_prepacked",
+    "w4a16_geglu_linear_prepacked",
     "w4a16_status_string",
     "w4a16_last_error",
     "w4a16_abi_version",
@@ -56,6 +60,14 @@ def load() -> ctypes.CDLL:
     lib.w4a16_linear.restype = ctypes.c_int
     lib.w4a16_geglu_linear.argtypes = [P, I, I, P, P, I, P, P, P]
     lib.w4a16_geglu_linear.restype = ctypes.c_int
+    lib.w4a16_prepacked_bytes.argtypes = [I, I]
+    lib.w4a16_prepacked_bytes.restype = ctypes.c_int64
+    lib.w4a16_prepack.argtypes = [P, I, I, P, P]
+    lib.w4a16_prepack.restype = ctypes.c_int
+    lib.w4a16_linear_prepacked.argtypes = [P, I, I, P, P, I, P, P, P]
+    lib.w4a16_linear_prepacked.restype = ctypes.c_int
+    lib.w4a16_geglu_linear_prepacked.argtypes = [P, I, I, P, P, I, P, P, P]
+    lib.w4a16_geglu_linear_prepacked.restype = ctypes.c_int
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_last_error.argtypes = []

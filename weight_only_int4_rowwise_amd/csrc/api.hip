@@ -10,10 +10,13 @@ namespace w4a16 {
 hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
                            hipStream_t stream);
 hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, bool geglu, hipStream_t stream);
+                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
+                         hipStream_t stream);
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          hipStream_t stream);
+                          bool tiled, hipStream_t stream);
+int64_t prepacked_bytes(int64_t n, int64_t k);
+hipError_t launch_prepack(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
 }  // namespace w4a16
 
 namespace {
@@ -65,7 +68,8 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
 }
 
 w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, const void *s,
-                        int64_t n_out, const void *bias, void *y, bool geglu, void *stream)
+                        int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
+                        void *stream)
 {
     const int64_t rows = geglu ? 2 * n_out : n_out;
     w4a16_status st = check_gemm_shape(m, k, rows);
@@ -79,9 +83,9 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (m <= kDecodeMaxM)
-        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, hs);
+        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
     else
-        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, hs);
+        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, hs);
     return from_hip(e);
 }
 
@@ -108,7 +112,8 @@ w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k, const void *
                           const void *scales_fp16, int64_t n, const void *bias_fp16, void *y_fp16,
                           void *stream)
 {
-    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, stream);
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, false,
+                      stream);
 }
 
 w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const void *q_packed,
@@ -117,7 +122,50 @@ w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const 
 {
     if (f > kMaxDim / 2)
         return W4A16_ERR_SHAPE;
-    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, stream);
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, false,
+                      stream);
+}
+
+int64_t w4a16_prepacked_bytes(int64_t n, int64_t k)
+{
+    if (n < 0 || k <= 0 || k % 32 != 0 || n > kMaxDim || k > kMaxDim)
+        return -1;
+    return w4a16::prepacked_bytes(n, k);
+}
+
+w4a16_status w4a16_prepack(const void *q_packed, int64_t n, int64_t k, void *q_prepacked,
+                           void *stream)
+{
+    if (w4a16_prepacked_bytes(n, k) < 0)
+        return W4A16_ERR_SHAPE;
+    if (n == 0)
+        return W4A16_OK;
+    if (!q_packed || !q_prepacked)
+        return W4A16_ERR_NULL;
+    if (!aligned16(q_packed) || !aligned16(q_prepacked))
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_prepack(q_packed, n, k, q_prepacked,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status w4a16_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                    const void *q_prepacked, const void *scales_fp16, int64_t n,
+                                    const void *bias_fp16, void *y_fp16, void *stream)
+{
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, n, bias_fp16, y_fp16, false, true,
+                      stream);
+}
+
+w4a16_status w4a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                          const void *q_prepacked, const void *scales_fp16,
+                                          int64_t f, const void *bias_fp16, void *y_fp16,
+                                          void *stream)
+{
+    // the gate / value boundary must fall on a 16-row tile boundary
+    if (f > kMaxDim / 2 || f % 16 != 0)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true,
+                      stream);
 }
 
 const char *w4a16_status_string(int status)

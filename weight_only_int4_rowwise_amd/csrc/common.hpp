@@ -22,17 +22,20 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------------------
 // INT4 -> FP16 dequantization of one dword (8 codes) into one MFMA operand.
 //
-// Flipping bit 3 of each nibble turns the two's-complement code q into the
-// offset-binary u = q + 8 in [1, 15].  OR-ing u into the mantissa of a
+// Flipping bit 3 of a nibble turns the two's-complement code q into the
+// offset-binary u = q + 8 in [1, 15].  Placing u in the mantissa of a
 // binary16 with a fixed exponent gives an exact value:
 //   0x6400 | u         = 1024 + u   (mantissa ulp 1 at exponent 10)
 //   0x5400 | (u << 4)  =   64 + u   (mantissa bit 4 worth 1 at exponent 6)
-// so one AND-OR forms two halves, and one packed f16 subtract of 1032 or 72
-// returns q exactly.  The four packed dwords hold the codes of byte offsets
-// (k0,k4) (k1,k5) (k2,k6) (k3,k7): element e of the operand is code
-// kPerm[e] of the dword.  The other operand is permuted the same way, and
-// since a dot product does not depend on the order of its terms the result
-// is unchanged.
+// and one packed f16 subtract of 1032 or 72 returns q exactly.  The flip,
+// the nibble mask and the exponent bits fold into one 3-input bit op:
+//   ((w ^ 0x8888...) & M) | C  ==  (w & M) ^ B,   B = (0x8888... & M) | C
+// since C has no bits inside M.  So 8 codes cost 9 VALU ops: one shift,
+// four v_bitop3_b32, four v_pk_add_f16.  The four packed dwords hold the
+// codes of byte offsets (k0,k4) (k1,k5) (k2,k6) (k3,k7): element e of the
+// operand is code kPerm[e] of the dword.  The other operand is permuted
+// the same way, and since a dot product does not depend on the order of
+// its terms the result is unchanged.
 // ---------------------------------------------------------------------------
 __device__ constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
@@ -43,20 +46,21 @@ __device__ __forceinline__ half2v bits_to_h2(uint32_t v)
 
 __device__ __forceinline__ half8 dequant8(uint32_t packed)
 {
-    const uint32_t u = packed ^ 0x88888888u;
-    const uint32_t u8 = u >> 8;
+    const uint32_t w8 = packed >> 8;
     const half2v lo_bias = {(_Float16)1032.0f, (_Float16)1032.0f};
     const half2v hi_bias = {(_Float16)72.0f, (_Float16)72.0f};
-    half2v p0 = bits_to_h2((u & 0x000F000Fu) | 0x64006400u) - lo_bias;   // k0, k4
-    half2v p1 = bits_to_h2((u & 0x00F000F0u) | 0x54005400u) - hi_bias;   // k1, k5
-    half2v p2 = bits_to_h2((u8 & 0x000F000Fu) | 0x64006400u) - lo_bias;  // k2, k6
-    half2v p3 = bits_to_h2((u8 & 0x00F000F0u) | 0x54005400u) - hi_bias;  // k3, k7
-    half8 r;
-    r[0] = p0[0]; r[1] = p0[1];
-    r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1];
-    r[6] = p3[0]; r[7] = p3[1];
-    return r;
+    // low nibbles: mask 0x000F000F, exponent 0x6400, flip 0x0008
+    // high nibbles: mask 0x00F000F0, exponent 0x5400, flip 0x0080
+    const half2v p0 = bits_to_h2((packed & 0x000F000Fu) ^ 0x64086408u) - lo_bias;   // k0, k4
+    const half2v p1 = bits_to_h2((packed & 0x00F000F0u) ^ 0x54805480u) - hi_bias;   // k1, k5
+    const half2v p2 = bits_to_h2((w8 & 0x000F000Fu) ^ 0x64086408u) - lo_bias;       // k2, k6
+    const half2v p3 = bits_to_h2((w8 & 0x00F000F0u) ^ 0x54805480u) - hi_bias;       // k3, k7
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, p0);
+    r[1] = __builtin_bit_cast(uint32_t, p1);
+    r[2] = __builtin_bit_cast(uint32_t, p2);
+    r[3] = __builtin_bit_cast(uint32_t, p3);
+    return __builtin_bit_cast(half8, r);
 }
 
 // Eight consecutive fp16 activations (as four dwords, natural order) into
@@ -89,6 +93,77 @@ __device__ __forceinline__ float4v mfma16x16x32(half8 a, half8 b, float4v c)
 __device__ __forceinline__ u32x4 load_stream16(const uint8_t *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Range-checked buffer loads.  A buffer resource carries the byte size of
+// the tensor; a load whose 16 bytes lie past it returns zeros without
+// touching memory.  Kernels point padding lanes (rows or reduction indices
+// past the end) at kOutOfRange instead of branching around the load, so
+// every load is unconditional and the compiler can keep loads of later
+// pipeline stages in flight across the current one.  Offsets are 32-bit:
+// the library rejects tensors of 2 GiB or more.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    // dword 3 = 0x00020000: 32-bit data format, the raw (stride 0) buffer
+    // setting for gfx9-family matrix-core GPUs
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// plain (cached) 16-byte load
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// streaming 16-byte load (non-temporal: weights are read once per call)
+__device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+
+// Byte offset of the 16 packed bytes (32 codes, reduction indices
+// [kc, kc + 32)) that lane `lane` of an MFMA A operand holds for weight
+// `row`; the lane's row is row % 16 == lane % 16 and kc % 128 == 32 (lane / 16).
+//  row-major layout: [n][k/2] bytes.
+//  prepacked layout: 16-row x 128-index tiles of 1 KB, tiles ordered by row
+//  group then by reduction position, lane l's 16 bytes at offset 16 l.
+template <bool TILED>
+__device__ __forceinline__ uint32_t piece_off(int64_t row, int64_t kc, int64_t row_bytes,
+                                              int64_t tiles_per_group, int lane)
+{
+    if (TILED)
+        return (uint32_t)(((row >> 4) * tiles_per_group + (kc >> 7)) * 1024 + 16 * lane);
+    return (uint32_t)(row * row_bytes + (kc >> 1));
+}
+
+// Per-lane base offset of weight `row` (kOutOfRange for padding rows) and
+// the offset step of the piece starting at reduction index kc, both 32-bit,
+// so that piece offsets are one add and one select (no branches).
+template <bool TILED>
+__device__ __forceinline__ uint32_t row_base_off(int64_t row, int64_t row_bytes,
+                                                 int64_t tiles_per_group, int lane)
+{
+    if (row < 0)
+        return kOutOfRange;
+    return TILED ? (uint32_t)((row >> 4) * tiles_per_group * 1024 + 16 * lane)
+                 : (uint32_t)(row * row_bytes);
+}
+
+template <bool TILED>
+__device__ __forceinline__ uint32_t piece_step_off(uint32_t kc)
+{
+    return TILED ? (kc >> 7) * 1024u : (kc >> 1);
+}
+
+// Bytes of a weight of `rows` rows in either layout.
+__host__ __device__ __forceinline__ int64_t weight_bytes(bool tiled, int64_t rows, int64_t k)
+{
+    return tiled ? ((rows + 15) / 16) * ((k + 127) / 128) * 1024 : rows * (k / 2);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p)

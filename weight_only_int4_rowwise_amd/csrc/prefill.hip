@@ -18,6 +18,9 @@
 //    into registers (one dwordx4, prefetched a step ahead) and dequantizes
 //    them into the MFMA A operand: the fp16 weight tile never exists in
 //    memory.  The scale is applied once per output in the epilogue.
+//  * All loads are unconditional range-checked buffer loads and the step
+//    loop is unrolled twice over two weight register sets, so the next
+//    step's loads stay in flight while this step's MFMAs run.
 #include "common.hpp"
 
 namespace w4a16 {
@@ -28,7 +31,7 @@ constexpr int kPBK = 128;           // reduction step
 constexpr int kPLd = kPBK + 8;      // LDS row stride in halves (272 bytes)
 constexpr int kPThreads = 256;
 
-template <bool GEGLU>
+template <bool GEGLU, bool TILED>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__restrict__ x,
                                                             int64_t m, int64_t k,
                                                             const uint8_t *__restrict__ packed,
@@ -52,9 +55,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
     constexpr int kOutPerTile = GEGLU ? kPBN / 2 : kPBN;
     const int64_t o0 = tile_n * kOutPerTile;
     const int64_t kb = k / 2;
+    const int64_t kt = (k + 127) / 128;   // tiles per row group (prepacked layout)
 
-    // weight row of this lane in group j (4 groups of 16 per wave), -1 past the end
-    int64_t row[4];
+    // base offset of the weight row of this lane in group j (4 groups of 16 per wave)
+    uint32_t wbase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         int64_t r;
@@ -67,8 +71,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
             r = o0 + 64 * wn + 16 * j + r16;
             ok = r < n_out;
         }
-        row[j] = ok ? r : -1;
+        wbase[j] = row_base_off<TILED>(ok ? r : -1, kb, kt, lane);
     }
+    const uint32_t k32 = (uint32_t)k;
 
     float4v acc[4][4];
 #pragma unroll
@@ -78,20 +83,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
             acc[j][b] = float4v{0.f, 0.f, 0.f, 0.f};
 
     const int64_t nsteps = (k + kPBK - 1) / kPBK;
+    const int64_t rows = GEGLU ? 2 * n_out : n_out;
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m * k * 2);
 
-    // activation copy: 128 rows x 16 chunks of 16 bytes; thread handles 8 chunks
+    // activation copy: 128 rows x 16 pieces of 16 bytes; thread handles 8
+    // pieces.  Issued before the same stage's weight loads: loads retire in
+    // order, so storing them to LDS does not wait for the weights.
     u32x4 xr[8];
+    uint32_t xrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + kPThreads * i;
+        const int64_t mi = m0 + c / 16;
+        xrow[i] = mi < m ? (uint32_t)((mi * k + 8 * (c % 16)) * 2) : kOutOfRange;
+    }
     auto load_x = [&](int64_t s) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = threadIdx.x + kPThreads * i;
-            const int rr = c / 16;
-            const int64_t kk = s * kPBK + 8 * (c % 16);
-            const int64_t mi = m0 + rr;
-            if (s < nsteps && mi < m && kk < k)
-                xr[i] = load16(x + mi * k + kk);
-            else
-                xr[i] = u32x4{0u, 0u, 0u, 0u};
+            const uint32_t kk = (uint32_t)s * kPBK + 8 * (c % 16);
+            xr[i] = buf_load16(xrs, kk < k32 ? xrow[i] + 2 * (uint32_t)s * kPBK : kOutOfRange);
         }
     };
     auto store_x = [&](int buf) {
@@ -102,29 +114,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
             *reinterpret_cast<u32x4 *>(&xs[buf][rr * kPLd + 8 * (c % 16)]) = permute_x8(xr[i]);
         }
     };
-    u32x4 wv[4];
     auto load_w = [&](int64_t s, u32x4(&wd)[4]) {
-        const int64_t kc = s * kPBK + 32 * g;
-        const bool kin = (s < nsteps) && (kc < k);
+        const uint32_t kc = (uint32_t)s * kPBK + 32 * g;
+        const uint32_t step = piece_step_off<TILED>(kc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (kin && row[j] >= 0)
-                wd[j] = load_stream16(packed + row[j] * kb + kc / 2);
-            else
-                wd[j] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < 4; ++j)
+            wd[j] = buf_load16_stream(wrs, kc < k32 ? wbase[j] + step : kOutOfRange);
     };
-
-    load_x(0);
-    load_w(0, wv);
-    store_x(0);
-    __syncthreads();
-
-    for (int64_t s = 0; s < nsteps; ++s) {
-        const int buf = (int)(s & 1);
-        u32x4 wn_[4];
-        load_x(s + 1);
-        load_w(s + 1, wn_);
+    auto compute = [&](int buf, const u32x4(&wd)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             half8 bx[4];
@@ -135,17 +132,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const half8 a = dequant8(wv[j][t]);
+                const half8 a = dequant8(wd[j][t]);
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     acc[j][b] = mfma16x16x32(a, bx[b], acc[j][b]);
             }
         }
-        store_x(buf ^ 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wv[j] = wn_[j];
+    };
+
+    // two register sets for the weights, used alternately (the loop is
+    // unrolled twice so no set is ever copied)
+    u32x4 wa[4], wb[4];
+    load_x(0);
+    load_w(0, wa);
+    store_x(0);
+    __syncthreads();
+    for (int64_t s = 0;;) {
+        load_x(s + 1);
+        load_w(s + 1, wb);
+        compute(0, wa);
+        store_x(1);
         __syncthreads();
+        if (++s >= nsteps)
+            break;
+        load_x(s + 1);
+        load_w(s + 1, wa);
+        compute(1, wb);
+        store_x(0);
+        __syncthreads();
+        if (++s >= nsteps)
+            break;
     }
 
     // epilogue: lane holds D[4 g + i][r16] of tile (j, b): weight row 4 g + i, token r16
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
 
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          hipStream_t stream)
+                          bool tiled, hipStream_t stream)
 {
     const int64_t out_per = geglu ? kPBN / 2 : kPBN;
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
@@ -202,12 +218,18 @@ hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packe
     const uint16_t *sp = static_cast<const uint16_t *>(scales);
     const uint16_t *bp = static_cast<const uint16_t *>(bias);
     uint16_t *yp = static_cast<uint16_t *>(y);
-    if (geglu)
-        hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(kPThreads), 0, stream,
-                           xp, m, k, pp, sp, n_out, bp, yp, (int)tiles_m);
+#define W4_PREFILL(G, T)                                                                          \
+    hipLaunchKernelGGL((prefill_kernel<G, T>), dim3((unsigned)grid), dim3(kPThreads), 0, stream, xp, \
+                       m, k, pp, sp, n_out, bp, yp, (int)tiles_m)
+    if (geglu && tiled)
+        W4_PREFILL(true, true);
+    else if (geglu)
+        W4_PREFILL(true, false);
+    else if (tiled)
+        W4_PREFILL(false, true);
     else
-        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(kPThreads), 0, stream,
-                           xp, m, k, pp, sp, n_out, bp, yp, (int)tiles_m);
+        W4_PREFILL(false, false);
+#undef W4_PREFILL
     return hipGetLastError();
 }
 
