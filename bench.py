@@ -5,12 +5,15 @@
 
 Headline workload: the GLM-130B decode QKV projection, weight 36864 x 12288
 quantized INT4 row-wise (N(0, 0.02^2) weights), fp16 activations
-M in {1, 8, 32, 64}.  One step = one w4a16_linear launch per M (the memory-
-bound decode kernel).  The weights rotate over 5 independently drawn
+M in {1, 8, 32, 64}.  One step = one W4A16 linear launch per M (the memory-
+bound decode kernel) on the weights in the prepacked tile layout
+(w4a16_prepack, applied once at load time like the quantization itself;
+same bytes, reordered).  The weights rotate over 5 independently drawn
 matrices (1.13 GB of packed weights, over 4x the 256 MB last-level cache),
 so every launch streams its weights from HBM.  `value` is the algorithmic
 bytes of the step (packed weights + scales + activations + outputs) over
-its time: HBM GB/s.
+its time: HBM GB/s.  The same step on the row-major packed layout
+(w4a16_linear) is reported in `extra`.
 
 The same JSON line also carries, measured in the same run:
   roofline      the dominant decode launch against 8 TB/s HBM
@@ -77,13 +80,14 @@ def time_launches(torch, fn, reps, warm=2):
 
 
 def make_rotating(torch, w4, synth, n, k, dist, count, seed0, dev):
+    """count independently drawn weights: (row-major packed, scales, prepacked)."""
     qs = []
     for i in range(count):
         g = synth.generator(seed0 + i, dev)
         w = synth.weight(n, k, g, dist, dev)
         q, s = w4.quantize_rowwise_int4(w)
         del w
-        qs.append((q, s))
+        qs.append((q, s, w4.w4a16_prepack(q)))
     torch.cuda.synchronize()
     return qs
 
@@ -127,9 +131,9 @@ def main(argv=None):
 
     def step():
         for m in DECODE_MS:
-            q, s = qkv[it[0] % ROTATE]
+            _, s, qp = qkv[it[0] % ROTATE]
             it[0] += 1
-            w4.w4a16_linear(xs[m], q, s, y_out=ys[m])
+            w4.w4a16_linear_prepacked(xs[m], qp, s, y_out=ys[m])
 
     for _ in range(a.warmup):
         step()
@@ -146,22 +150,26 @@ def main(argv=None):
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"headline: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
-    # per-M launch durations (roofline of the dominant decode launch)
-    per_m = {}
+    # per-M launch durations (roofline of the dominant decode launch), both layouts
+    per_m, per_m_rm = {}, {}
     for m in DECODE_MS:
-        j = [0]
+        for layout, table in (("prepacked", per_m), ("row-major", per_m_rm)):
+            j = [0]
 
-        def one(m=m, j=j):
-            q, s = qkv[j[0] % ROTATE]
-            j[0] += 1
-            w4.w4a16_linear(xs[m], q, s, y_out=ys[m])
+            def one(m=m, j=j, layout=layout):
+                q, s, qp = qkv[j[0] % ROTATE]
+                j[0] += 1
+                if layout == "prepacked":
+                    w4.w4a16_linear_prepacked(xs[m], qp, s, y_out=ys[m])
+                else:
+                    w4.w4a16_linear(xs[m], q, s, y_out=ys[m])
 
-        t = time_launches(torch, one, 40)
-        b = linear_bytes(m, N, K, N)
-        per_m[m] = {"us": round(t * 1e6, 2), "bytes": b, "GBs": round(b / t / 1e9, 1),
-                    "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                    "mfma_frac_needed": round(2.0 * m * N * K / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
-        log(f"decode QKV M={m}: {t * 1e6:.1f} us, {b / t / 1e9:.0f} GB/s")
+            t = time_launches(torch, one, 40)
+            b = linear_bytes(m, N, K, N)
+            table[m] = {"us": round(t * 1e6, 2), "bytes": b, "GBs": round(b / t / 1e9, 1),
+                        "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac_needed": round(2.0 * m * N * K / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+            log(f"decode QKV M={m} {layout}: {t * 1e6:.1f} us, {b / t / 1e9:.0f} GB/s")
     dom = max(DECODE_MS, key=lambda m: per_m[m]["us"])
     mb = (dom + 15) // 16
     traffic = None
@@ -173,7 +181,8 @@ def main(argv=None):
             traffic = tr["bytes_per_launch"][str(dom)]
     roofline = {
         "bound": "hbm",
-        "kernel": f"decode_kernel (M={dom}, {mb} token block{'s' if mb > 1 else ''}), QKV 36864x12288",
+        "kernel": f"decode_kernel (M={dom}, {mb} token block{'s' if mb > 1 else ''}, prepacked), "
+                  "QKV 36864x12288",
         "achieved": per_m[dom]["GBs"],
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
@@ -188,7 +197,7 @@ def main(argv=None):
     if not a.no_cpu_baseline:
         import oracle
         rows = 2048
-        q0, s0 = qkv[0]
+        q0, s0, _ = qkv[0]
         p_host = q0[:rows].cpu().numpy()
         s_host = s0[:rows].cpu().view(torch.int16).numpy().view("uint16")
         tot_b, tot_t = 0, 0.0
@@ -206,7 +215,11 @@ def main(argv=None):
         log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads")
 
     # -------------------------------------------------------------- extra
-    extra = {"decode_qkv_per_m": {str(m): v for m, v in per_m.items()}}
+    tot_b = sum(per_m_rm[m]["bytes"] for m in DECODE_MS)
+    tot_t = sum(per_m_rm[m]["us"] for m in DECODE_MS) / 1e6
+    extra = {"decode_qkv_per_m": {str(m): v for m, v in per_m.items()},
+             "decode_qkv_row_major_per_m": {str(m): v for m, v in per_m_rm.items()},
+             "decode_qkv_row_major_step_GBs": round(tot_b / tot_t / 1e9, 1)}
     del ys
     if not a.no_extra:
         extra.update(extra_workloads(torch, w4, synth, dev, a))
@@ -226,7 +239,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": "GLM-130B decode QKV projection: INT4 row-wise weight 36864x12288 "
-                        "(N(0,0.02^2)), fp16 activations M in {1,8,32,64}, one launch per M per step",
+                        "(N(0,0.02^2)), fp16 activations M in {1,8,32,64}, one launch per M per step, "
+                        "weights in the prepacked tile layout",
             "N": N, "K": K, "M": list(DECODE_MS),
             "rotating_weight_buffers": ROTATE,
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -257,14 +271,14 @@ def extra_workloads(torch, w4, synth, dev, a):
         c = [0]
 
         def up(c=c, xu=xu, yu=yu):
-            q, s = ups[c[0] % len(ups)]
+            _, s, qp = ups[c[0] % len(ups)]
             c[0] += 1
-            w4.w4a16_geglu_linear(xu, q, s, y_out=yu)
+            w4.w4a16_geglu_linear_prepacked(xu, qp, s, y_out=yu)
 
         def down(c=c, xd=xd, yd=yd):
-            q, s = downs[c[0] % len(downs)]
+            _, s, qp = downs[c[0] % len(downs)]
             c[0] += 1
-            w4.w4a16_linear(xd, q, s, y_out=yd)
+            w4.w4a16_linear_prepacked(xd, qp, s, y_out=yd)
 
         tu = time_launches(torch, up, 30)
         td = time_launches(torch, down, 30)
@@ -282,22 +296,27 @@ def extra_workloads(torch, w4, synth, dev, a):
     attn = make_rotating(torch, w4, synth, H, H, "normal", 2, 300, dev)
     x = synth.activations(M, H, g, dev)
     pf = {}
+    def rec(t, fl):
+        return {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+
     y1 = torch.empty(M, H, dtype=torch.float16, device=dev)
-    t = time_launches(torch, lambda: w4.w4a16_linear(x, attn[0][0], attn[0][1], y_out=y1), 10)
     fl = 2.0 * M * H * H
-    pf["attn_out"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
-                      "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    pf["attn_out"] = rec(time_launches(
+        torch, lambda: w4.w4a16_linear_prepacked(x, attn[0][2], attn[0][1], y_out=y1), 10), fl)
+    pf["attn_out_row_major"] = rec(time_launches(
+        torch, lambda: w4.w4a16_linear(x, attn[0][0], attn[0][1], y_out=y1), 10), fl)
     del y1
     y2 = torch.empty(M, F, dtype=torch.float16, device=dev)
-    t = time_launches(torch, lambda: w4.w4a16_geglu_linear(x, ups[0][0], ups[0][1], y_out=y2), 5)
     fl = 2.0 * M * 2 * F * H
-    pf["ffn_up_geglu"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
-                          "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    pf["ffn_up_geglu"] = rec(time_launches(
+        torch, lambda: w4.w4a16_geglu_linear_prepacked(x, ups[0][2], ups[0][1], y_out=y2), 5), fl)
+    pf["ffn_up_geglu_row_major"] = rec(time_launches(
+        torch, lambda: w4.w4a16_geglu_linear(x, ups[0][0], ups[0][1], y_out=y2), 5), fl)
     del y2
     y3 = torch.empty(M, 2 * F, dtype=torch.float16, device=dev)
-    t = time_launches(torch, lambda: w4.w4a16_linear(x, ups[0][0], ups[0][1], y_out=y3), 5)
-    pf["ffn_up_plain"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
-                          "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    pf["ffn_up_plain"] = rec(time_launches(
+        torch, lambda: w4.w4a16_linear_prepacked(x, ups[0][2], ups[0][1], y_out=y3), 5), fl)
     del y3
     # the fp16 GEMM of the same shape through torch, as a context ceiling
     wf = synth.weight(H, H, g, device=dev)
@@ -337,8 +356,10 @@ def full_step(torch, w4, synth, dev):
         for mid, (name, n, k) in enumerate(synth.LAYER_LINEARS):
             g = synth.generator(synth.layer_weight_seed(l, mid), dev)
             w = synth.weight(n, k, g, device=dev)
-            mats.append(w4.quantize_rowwise_int4(w))
+            q, s = w4.quantize_rowwise_int4(w)
             del w
+            mats.append((w4.w4a16_prepack(q), s))
+            del q
         layers.append(mats)
     torch.cuda.synchronize()
     g = synth.generator(7, dev)
@@ -351,10 +372,10 @@ def full_step(torch, w4, synth, dev):
 
     def run():
         for mats in layers:
-            w4.w4a16_linear(xh, mats[0][0], mats[0][1], y_out=y_qkv)
-            w4.w4a16_linear(xh, mats[1][0], mats[1][1], y_out=y_h)
-            w4.w4a16_geglu_linear(xh, mats[2][0], mats[2][1], y_out=y_f)
-            w4.w4a16_linear(xf, mats[3][0], mats[3][1], y_out=y_h)
+            w4.w4a16_linear_prepacked(xh, mats[0][0], mats[0][1], y_out=y_qkv)
+            w4.w4a16_linear_prepacked(xh, mats[1][0], mats[1][1], y_out=y_h)
+            w4.w4a16_geglu_linear_prepacked(xh, mats[2][0], mats[2][1], y_out=y_f)
+            w4.w4a16_linear_prepacked(xf, mats[3][0], mats[3][1], y_out=y_h)
 
     t = time_launches(torch, run, 3, warm=1)
     total = 0

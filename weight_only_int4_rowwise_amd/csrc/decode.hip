@@ -5,7 +5,8 @@
 // run time; paperlayer.ai summary, "INT4 Quantization for RTX 3090s/2080s").
 // At decode sizes the packed weights dominate the traffic (k/2 bytes per
 // row against 2 m k bytes of activations), so both kernels here are built
-// to stream the weights from HBM once at full bandwidth:
+// to stream the weights from HBM once at full bandwidth (one kernel
+// template below, shaped per token count):
 //
 //  * Codes become exact fp16 integers in registers (dequant8: 1.25 VALU ops
 //    per code) and feed v_mfma_f32_16x16x32_f16 with 16 weight rows as the
@@ -29,51 +30,64 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 }
 
 // ---------------------------------------------------------------------------
-// Small-batch decode (m <= 16): one 16-token MFMA block.
+// Decode kernel (m <= 64).
 //
-// A workgroup of 4 wavefronts owns RG groups of 16 outputs; the KS = 4 / RG
-// wavefronts of a group split the reduction into interleaved chunks of
+// A wavefront owns NGW groups of 16 weight rows (for GeGLU: NGW / 2 gate
+// groups and the matching value groups) and MB blocks of 16 tokens.  A
+// workgroup of 4 wavefronts holds RG such row sets; the KS = 4 / RG
+// wavefronts of a row set split the reduction into interleaved chunks of
 // 128 KU indices.  A wavefront streams its rows chunk by chunk (KU 16-byte
-// pieces per lane per row), with a ring of D register sets so the pieces of
-// the next D - 1 chunks are in flight while the current one is multiplied.
-// The activation chunks of a round (KS chunks, MR x 128 KU fp16 each, MR =
-// m rounded up to 4, 8 or 16) are loaded once per workgroup, permuted into
-// the dequant8 operand order and double-buffered in LDS, one barrier per
-// round; the RG wavefronts that work on the same chunk share it.  Each
-// round's activation loads are issued before its weight loads: vector
-// loads retire in order, so waiting for the activations does not wait for
-// the weights.  Partial sums of the KS wavefronts of a group meet in LDS in
-// a fixed order.
+// pieces per lane per row group), with a ring of D register sets so the
+// pieces of the next D - 1 chunks are in flight while the current one is
+// multiplied.  Each dequantized A operand feeds MB MFMAs (one per token
+// block), and each activation operand read from LDS feeds NGW MFMAs.
 //
-// The dequantization is the bulk of the VALU work (10 ops per 8 codes), so
+// The activation chunks of a round (KS chunks, MR x 128 KU fp16 each; MR =
+// m rounded up to 4, 8 or 16 for one block, 16 MB otherwise) are loaded
+// once per workgroup, permuted into the dequant8 operand order and
+// double-buffered in LDS, one barrier per round; the RG wavefronts that
+// work on the same chunk share it.  Each round's activation loads are
+// issued before its weight loads: vector loads retire in order, so waiting
+// for the activations does not wait for the weights.  Partial sums of the
+// KS wavefronts of a row set meet in LDS in a fixed order.
+//
+// The dequantization is the bulk of the VALU work (9 ops per 8 codes), so
 // everything else is kept off the VALU: every lane's load offset is a
 // per-lane constant plus a wave-uniform step.  Rows past the end are
 // clamped to the last row and tokens past m to token m - 1 (they only feed
-// MFMA columns and rows that are never stored); a chunk past the end gets
+// MFMA rows and columns that are never stored); a chunk past the end gets
 // the out-of-range step, so its loads return zeros.  EVEN (k a multiple of
 // the 128 KU KS-index round) needs no per-lane reduction-index checks; the
 // general instantiation adds them for a ragged last round.
 //
 // TILED selects the prepacked weight layout (w4a16_prepack): each 16-row x
 // 128-index tile is one contiguous 1 KB block in lane order, so a
-// wavefront reads KU KB of consecutive memory per chunk instead of 16 row
-// segments of 64 KU bytes.
+// wavefront reads KU KB of consecutive memory per chunk and row group
+// instead of 16 row segments of 64 KU bytes.
 // ---------------------------------------------------------------------------
-template <int KU, int RG, int D, int MR, bool EVEN, bool GEGLU, bool TILED>
-__global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
+template <int MB, int MR>
+struct TokenTile {
+    static_assert(MB == 1 ? (MR == 4 || MR == 8 || MR == 16) : MR == 16 * MB, "token rows");
+};
+
+template <int KU, int RG, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+__global__ __launch_bounds__(4 * kWave) void decode_kernel(
     const uint16_t *__restrict__ x, int m, int64_t k, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, int64_t n_out, const uint16_t *__restrict__ bias,
     uint16_t *__restrict__ y)
 {
-    constexpr int NG = GEGLU ? 2 : 1;
+    (void)TokenTile<MB, MR>{};
+    static_assert(!GEGLU || NGW % 2 == 0, "GeGLU pairs gate and value row groups");
     constexpr int KS = 4 / RG;
     constexpr int KC = 128 * KU;              // reduction indices per chunk
     constexpr int LD = KC + 8;                // LDS row stride (halves): +16 bytes against bank conflicts
     constexpr int RP = KC / 8;                // 16-byte pieces per activation row per chunk
-    constexpr int NPC = KS * MR * RP;                // activation pieces per round
+    constexpr int NPC = KS * MR * RP;         // activation pieces per round
     constexpr int XP = (NPC + 4 * kWave - 1) / (4 * kWave);   // per thread
     static_assert(NPC % (4 * kWave) == 0 || NPC < 4 * kWave, "activation pieces must divide evenly");
     static_assert(D % 2 == 0, "the LDS double buffer alternates with the round parity");
+    constexpr int CH = MB == 1 ? 2 : 1;       // independent accumulator chains per (group, block)
+    constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;   // outputs per wave
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][KS][MR][LD];
 
     const int lane = threadIdx.x % kWave;
@@ -82,7 +96,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
     const int kp = wave / RG;
     const int r16 = lane % 16;
     const int g = lane / 16;
-    const int64_t o0 = ((int64_t)blockIdx.x * RG + rgi) * 16;   // first output of this group
+    const int64_t o0 = ((int64_t)blockIdx.x * RG + rgi) * OUTW;   // first output of this wave
     const int64_t kb = k / 2;
     const int64_t kt = ceil_div(k, 128);
 
@@ -90,29 +104,30 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (int64_t)m * k * 2);
 
-    // Per-lane constant part of each weight load offset.  Output rows past
-    // n_out: the prepacked layout holds zero rows there; the row-major one
-    // is clamped to the last row (the result is never stored).
-    uint32_t wbase[NG];
-    {
-        int64_t o = o0 + r16;
+    // Per-lane constant part of each weight load offset.  Rows past the
+    // end: the prepacked layout holds zero rows there (or reads past the
+    // buffer, which return zeros); the row-major one is clamped to the last
+    // row (the result is never stored).
+    uint32_t wbase[NGW];
+#pragma unroll
+    for (int j = 0; j < NGW; ++j) {
+        int64_t o = GEGLU ? o0 + 16 * (j % (NGW / 2)) + r16 : o0 + 16 * j + r16;
         if (!TILED && o >= n_out)
             o = n_out - 1;
-        wbase[0] = TILED ? (uint32_t)((o >> 4) * kt * 1024 + 16 * lane)
-                         : (uint32_t)(o * kb + 16 * g);
-        if (GEGLU) {
-            const int64_t ov = n_out + o;
-            wbase[NG - 1] = TILED ? (uint32_t)((ov >> 4) * kt * 1024 + 16 * lane)
-                                  : (uint32_t)(ov * kb + 16 * g);
-        }
+        const int64_t row = (GEGLU && j >= NGW / 2) ? n_out + o : o;
+        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 + 16 * lane)
+                         : (uint32_t)(row * kb + 16 * g);
     }
     const uint32_t k32 = (uint32_t)k;
 
-    // two independent accumulator chains per group (even / odd pieces)
-    float4v acc[NG][2];
+    float4v acc[NGW][MB][CH];
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
-        acc[j][0] = acc[j][1] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NGW; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                acc[j][b][c] = float4v{0.f, 0.f, 0.f, 0.f};
 
     const int64_t nch = ceil_div(k, KC);
     const int64_t rounds = ceil_div(nch, KS);
@@ -120,7 +135,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
     // Chunk c of this wave, piece p: reduction indices c KC + 128 p + 32 g.
     // The wave-uniform step (c KC + 128 p) / 2 bytes (row-major) or tile
     // c KU + p (prepacked) is added to the per-lane base.
-    auto load_w = [&](int64_t r, u32x4(&wd)[NG][KU]) {
+    auto load_w = [&](int64_t r, u32x4(&wd)[NGW][KU]) {
         const uint32_t c = (uint32_t)(r * KS + kp);
         const bool live = c < (uint32_t)nch;
 #pragma unroll
@@ -130,7 +145,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
             if (!live)
                 step = kOutOfRange;
 #pragma unroll
-            for (int j = 0; j < NG; ++j) {
+            for (int j = 0; j < NGW; ++j) {
                 uint32_t off = wbase[j] + step;
                 if (!EVEN && !TILED && u + 32 * g >= k32)
                     off = kOutOfRange;                 // ragged last piece, row-major only
@@ -170,16 +185,23 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
         }
     };
     const int brow = r16 < MR ? r16 : MR - 1;          // MFMA columns past MR repeat row MR - 1
-    auto compute = [&](int buf, const u32x4(&wd)[NG][KU]) {
-        const uint16_t *xb = &xs[buf][kp][brow][32 * g];
+    auto compute = [&](int buf, const u32x4(&wd)[NGW][KU]) {
 #pragma unroll
         for (int p = 0; p < KU; ++p)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const half8 bx = as_half8(*reinterpret_cast<const u32x4 *>(xb + 128 * p + 8 * t));
+                half8 bx[MB];
 #pragma unroll
-                for (int j = 0; j < NG; ++j)
-                    acc[j][t & 1] = mfma16x16x32(dequant8(wd[j][p][t]), bx, acc[j][t & 1]);
+                for (int b = 0; b < MB; ++b)
+                    bx[b] = as_half8(*reinterpret_cast<const u32x4 *>(
+                        &xs[buf][kp][16 * b + brow][32 * g + 128 * p + 8 * t]));
+#pragma unroll
+                for (int j = 0; j < NGW; ++j) {
+                    const half8 a = dequant8(wd[j][p][t]);
+#pragma unroll
+                    for (int b = 0; b < MB; ++b)
+                        acc[j][b][t % CH] = mfma16x16x32(a, bx[b], acc[j][b][t % CH]);
+                }
             }
     };
 
@@ -187,7 +209,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
     // rounds earlier.  The round loop is unrolled D times so every set has
     // a fixed register name (no copies, which would force the loads to
     // retire early).
-    u32x4 wr[D][NG][KU];
+    u32x4 wr[D][NGW][KU];
     load_x(0);
 #pragma unroll
     for (int i = 0; i < D - 1; ++i)
@@ -207,21 +229,29 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
             __syncthreads();
         }
     }
+    if (CH > 1) {
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
-        acc[j][0] += acc[j][1];
+        for (int j = 0; j < NGW; ++j)
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                acc[j][b][0] += acc[j][b][CH - 1];
+    }
 
     if (KS > 1) {
         // partial sums of K-parts 1..KS-1 -> LDS; K-part 0 adds them in order
-        static_assert(sizeof(xs) >= (KS - 1) * RG * NG * kWave * 4 * sizeof(float),
+        constexpr int kSlot = NGW * MB * kWave * 4;   // floats per wave
+        static_assert(sizeof(xs) >= (KS - 1) * RG * kSlot * sizeof(float),
                       "reduction slots reuse the activation buffer");
         float *red = reinterpret_cast<float *>(&xs[0][0][0][0]);
         if (kp > 0) {
 #pragma unroll
-            for (int j = 0; j < NG; ++j)
+            for (int j = 0; j < NGW; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[((((kp - 1) * RG + rgi) * NG + j) * kWave + lane) * 4 + i] = acc[j][0][i];
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[((kp - 1) * RG + rgi) * kSlot + ((j * MB + b) * kWave + lane) * 4 + i] =
+                            acc[j][b][0][i];
         }
         __syncthreads();
         if (kp > 0)
@@ -229,309 +259,122 @@ __global__ __launch_bounds__(4 * kWave) void decode_small_kernel(
 #pragma unroll
         for (int q = 1; q < KS; ++q)
 #pragma unroll
-            for (int j = 0; j < NG; ++j)
+            for (int j = 0; j < NGW; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[j][0][i] += red[((((q - 1) * RG + rgi) * NG + j) * kWave + lane) * 4 + i];
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[j][b][0][i] +=
+                            red[((q - 1) * RG + rgi) * kSlot + ((j * MB + b) * kWave + lane) * 4 + i];
     }
 
-    // lane holds D[4 g + i][r16]: output o0 + 4 g + i, token r16
-    if (r16 < m) {
+    // lane holds D[4 g + i][r16] of (row group j, token block b):
+    // output row 4 g + i of the group, token 16 b + r16
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t o = o0 + 4 * g + i;
-            if (o >= n_out)
-                continue;
-            float v;
-            if (GEGLU) {
-                float a = acc[0][0][i] * half_bits_to_float(scales[o]);
-                float bv = acc[NG - 1][0][i] * half_bits_to_float(scales[n_out + o]);
-                if (bias) {
-                    a += half_bits_to_float(bias[o]);
-                    bv += half_bits_to_float(bias[n_out + o]);
+    for (int b = 0; b < MB; ++b) {
+        const int mi = 16 * b + r16;
+        if (mi >= m)
+            continue;
+        constexpr int NO = GEGLU ? NGW / 2 : NGW;   // output groups
+#pragma unroll
+        for (int j = 0; j < NO; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t o = o0 + 16 * j + 4 * g + i;
+                if (o >= n_out)
+                    continue;
+                float v;
+                if (GEGLU) {
+                    float a = acc[j][b][0][i] * half_bits_to_float(scales[o]);
+                    float bv = acc[j + NO][b][0][i] * half_bits_to_float(scales[n_out + o]);
+                    if (bias) {
+                        a += half_bits_to_float(bias[o]);
+                        bv += half_bits_to_float(bias[n_out + o]);
+                    }
+                    v = gelu_erf(a) * bv;
+                } else {
+                    v = acc[j][b][0][i] * half_bits_to_float(scales[o]);
+                    if (bias)
+                        v += half_bits_to_float(bias[o]);
                 }
-                v = gelu_erf(a) * bv;
-            } else {
-                v = acc[0][0][i] * half_bits_to_float(scales[o]);
-                if (bias)
-                    v += half_bits_to_float(bias[o]);
+                y[(int64_t)mi * n_out + o] = float_to_half_bits(v);
             }
-            y[(int64_t)r16 * n_out + o] = float_to_half_bits(v);
-        }
     }
 }
 
-template <int KU, int RG, int D, int MR, bool EVEN, bool GEGLU, bool TILED>
-void launch_decode_small_t(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                           int64_t n_out, const void *bias, void *y, hipStream_t stream)
+template <int KU, int RG, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+void launch_decode_t(const void *x, int m, int64_t k, const void *packed, const void *scales,
+                     int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)ceil_div(n_out, 16 * RG);
-    hipLaunchKernelGGL((decode_small_kernel<KU, RG, D, MR, EVEN, GEGLU, TILED>), dim3(grid),
+    constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;
+    const unsigned grid = (unsigned)ceil_div(n_out, OUTW * RG);
+    hipLaunchKernelGGL((decode_kernel<KU, RG, D, MB, MR, NGW, EVEN, GEGLU, TILED>), dim3(grid),
                        dim3(4 * kWave), 0, stream, static_cast<const uint16_t *>(x), m, k,
                        static_cast<const uint8_t *>(packed), static_cast<const uint16_t *>(scales),
                        n_out, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
 }
 
-// Token-count class and reduction evenness of a small-batch launch.
-template <int KU, int RG, int D, bool GEGLU, bool TILED>
-void launch_decode_small(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, hipStream_t stream)
-{
-    const bool even = k % (128 * KU * (4 / RG)) == 0;
-#define W4_SMALL(MR, EV)                                                                          \
-    launch_decode_small_t<KU, RG, D, MR, EV, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, \
-                                                           stream)
-    if (m <= 4) {
-        if (even) W4_SMALL(4, true); else W4_SMALL(4, false);
-    } else if (m <= 8) {
-        if (even) W4_SMALL(8, true); else W4_SMALL(8, false);
-    } else {
-        if (even) W4_SMALL(16, true); else W4_SMALL(16, false);
-    }
-#undef W4_SMALL
-}
-
-// ---------------------------------------------------------------------------
-// Mid-batch decode (16 < m <= 64): MB 16-token blocks per MFMA row group.
-//
-// A workgroup owns 16 NG weight rows; its W wavefronts split the reduction
-// into 128 KU-wide steps taken round-robin, so the waves of a workgroup
-// sweep each row front to back together.  Per step a lane loads KU
-// 16-byte pieces of each of its NG rows and the matching 4 KU x 16 bytes of
-// its activation row; the next step's loads are in flight while the
-// current step runs.  The W partial sums meet in LDS in a fixed order.
-// ---------------------------------------------------------------------------
-template <int MB, int NG, int W, int KU, bool GEGLU, bool TILED>
-__global__ __launch_bounds__(W * kWave) void decode_kernel(const uint16_t *__restrict__ x, int m,
-                                                          int64_t k,
-                                                          const uint8_t *__restrict__ packed,
-                                                          const uint16_t *__restrict__ scales,
-                                                          int64_t n_out,
-                                                          const uint16_t *__restrict__ bias,
-                                                          uint16_t *__restrict__ y)
-{
-    static_assert(!GEGLU || (NG % 2 == 0), "GeGLU tiles pair gate and value groups");
-    constexpr int kRowsPerWG = 16 * NG;
-    constexpr int kOutPerWG = GEGLU ? kRowsPerWG / 2 : kRowsPerWG;
-    constexpr int kStep = 128 * KU;          // reduction indices per wave step
-    constexpr int kRed = W / 2;              // partial-sum slots (two waves per slot)
-    __shared__ float red[kRed][NG][MB][kWave][4];
-
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    const int r16 = lane % 16;
-    const int g = lane / 16;
-    const int64_t out0 = (int64_t)blockIdx.x * kOutPerWG;
-    const int64_t kb = k / 2;
-    const int64_t kt = ceil_div(k, 128);
-
-    const int64_t rows = GEGLU ? 2 * n_out : n_out;
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (int64_t)m * k * 2);
-
-    // base offset of the weight row held by this lane for group j
-    uint32_t wbase[NG];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        int64_t r;
-        bool ok;
-        if (GEGLU) {
-            const int jj = j % (NG / 2);
-            const int64_t f = out0 + 16 * jj + r16;
-            ok = f < n_out;
-            r = (j < NG / 2) ? f : n_out + f;
-        } else {
-            r = out0 + 16 * j + r16;
-            ok = r < n_out;
-        }
-        wbase[j] = row_base_off<TILED>(ok ? r : -1, kb, kt, lane);
-    }
-    uint32_t xbase[MB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b) {
-        const int mi = 16 * b + r16;
-        xbase[b] = mi < m ? (uint32_t)(mi * k * 2) : kOutOfRange;
-    }
-    const uint32_t k32 = (uint32_t)k;
-
-    float4v acc[NG][MB];
-#pragma unroll
-    for (int j = 0; j < NG; ++j)
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-            acc[j][b] = float4v{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t nsteps = ceil_div(k, kStep);
-
-    // Piece p of a step: bytes [64 p + 16 g, +16) of the row's 64 KU-byte
-    // chunk, i.e. reduction indices [128 p + 32 g, +32).
-    auto load_step = [&](int64_t s, u32x4(&wd)[NG][KU], u32x4(&xd)[MB][KU][4]) {
-#pragma unroll
-        for (int p = 0; p < KU; ++p) {
-            const uint32_t kc = (uint32_t)s * kStep + 128 * p + 32 * g;
-            const bool kin = kc < k32;
-#pragma unroll
-            for (int b = 0; b < MB; ++b)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    xd[b][p][t] = buf_load16(xrs, kin ? xbase[b] + 2 * (kc + 8 * t) : kOutOfRange);
-            const uint32_t step = piece_step_off<TILED>(kc);
-#pragma unroll
-            for (int j = 0; j < NG; ++j)
-                wd[j][p] = buf_load16_stream(wrs, kin ? wbase[j] + step : kOutOfRange);
-        }
-    };
-    auto compute = [&](const u32x4(&wd)[NG][KU], const u32x4(&xd)[MB][KU][4]) {
-#pragma unroll
-        for (int p = 0; p < KU; ++p)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                half8 bx[MB];
-#pragma unroll
-                for (int b = 0; b < MB; ++b)
-                    bx[b] = as_half8(permute_x8(xd[b][p][t]));
-#pragma unroll
-                for (int j = 0; j < NG; ++j) {
-                    const half8 a = dequant8(wd[j][p][t]);
-#pragma unroll
-                    for (int b = 0; b < MB; ++b)
-                        acc[j][b] = mfma16x16x32(a, bx[b], acc[j][b]);
-                }
-            }
-    };
-
-    u32x4 wa[NG][KU], xa[MB][KU][4], wb[NG][KU], xb[MB][KU][4];
-    int64_t s = wave;
-    load_step(s, wa, xa);
-    while (s < nsteps) {
-        load_step(s + W, wb, xb);
-        compute(wa, xa);
-        s += W;
-        if (s >= nsteps)
-            break;
-        load_step(s + W, wa, xa);
-        compute(wb, xb);
-        s += W;
-    }
-
-    // Partial sums of the W waves meet in LDS in a fixed order: the upper
-    // half of the waves stores, the lower half adds its own sum on top, and
-    // the epilogue adds the W / 2 slots.
-    if (wave >= kRed) {
-#pragma unroll
-        for (int j = 0; j < NG; ++j)
-#pragma unroll
-            for (int b = 0; b < MB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[wave - kRed][j][b][lane][i] = acc[j][b][i];
-    }
-    __syncthreads();
-    if (wave < kRed) {
-#pragma unroll
-        for (int j = 0; j < NG; ++j)
-#pragma unroll
-            for (int b = 0; b < MB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[wave][j][b][lane][i] = acc[j][b][i] + red[wave][j][b][lane][i];
-    }
-    __syncthreads();
-
-    // D[4 (l / 16) + i][l % 16]: weight row 4 (l / 16) + i of the group, token l % 16
-    auto partial = [&](int j, int rr, int mi) {
-        const int b = mi / 16;
-        const int l = 16 * (rr / 4) + (mi % 16);
-        const int i = rr % 4;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < kRed; ++w)
-            v += red[w][j][b][l][i];
-        return v;
-    };
-
-    const int total = kOutPerWG * m;
-    for (int idx = threadIdx.x; idx < total; idx += W * kWave) {
-        const int col = idx % kOutPerWG;
-        const int mi = idx / kOutPerWG;
-        const int64_t o = out0 + col;
-        if (o >= n_out)
-            continue;
-        const int j = col / 16;
-        const int rr = col % 16;
-        float val;
-        if (GEGLU) {
-            float a = partial(j, rr, mi) * half_bits_to_float(scales[o]);
-            float bv = partial(j + NG / 2, rr, mi) * half_bits_to_float(scales[n_out + o]);
-            if (bias) {
-                a += half_bits_to_float(bias[o]);
-                bv += half_bits_to_float(bias[n_out + o]);
-            }
-            val = gelu_erf(a) * bv;
-        } else {
-            val = partial(j, rr, mi) * half_bits_to_float(scales[o]);
-            if (bias)
-                val += half_bits_to_float(bias[o]);
-        }
-        y[(int64_t)mi * n_out + o] = float_to_half_bits(val);
-    }
-}
-
-template <int MB, int NG, int W, int KU, bool GEGLU, bool TILED>
-void launch_decode_t(const void *x, int m, int64_t k, const void *packed, const void *scales,
+// Reduction evenness of a launch.
+template <int KU, int RG, int D, int MB, int MR, int NGW, bool GEGLU, bool TILED>
+void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const void *scales,
                      int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
-    constexpr int out_per = GEGLU ? 8 * NG : 16 * NG;
-    const unsigned grid = (unsigned)ceil_div(n_out, out_per);
-    hipLaunchKernelGGL((decode_kernel<MB, NG, W, KU, GEGLU, TILED>), dim3(grid), dim3(W * kWave), 0,
-                       stream, static_cast<const uint16_t *>(x), m, k,
-                       static_cast<const uint8_t *>(packed), static_cast<const uint16_t *>(scales),
-                       n_out, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
-}
-
-template <int MB, bool GEGLU, bool TILED>
-static void launch_decode_mb(const void *x, int m, int64_t k, const void *packed,
-                             const void *scales, int64_t n_out, const void *bias, void *y,
-                             hipStream_t stream)
-{
-    // Enough workgroups to cover all 256 compute units several times over,
-    // with as many rows per workgroup as that allows (fewer activation
-    // re-reads per weight byte).
-    const int64_t rows = GEGLU ? 2 * n_out : n_out;
-    if (rows / 64 >= 512)
-        launch_decode_t<MB, 4, 4, 1, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    if (k % (128 * KU * (4 / RG)) == 0)
+        launch_decode_t<KU, RG, D, MB, MR, NGW, true, GEGLU, TILED>(x, m, k, packed, scales, n_out,
+                                                                    bias, y, stream);
     else
-        launch_decode_t<MB, 2, 4, 1, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+        launch_decode_t<KU, RG, D, MB, MR, NGW, false, GEGLU, TILED>(x, m, k, packed, scales,
+                                                                     n_out, bias, y, stream);
 }
 
-template <bool TILED>
+// Launch shapes per token class and weight height (rows = n, or 2 f for
+// GeGLU), from sweeps over KU, RG, D and NGW on MI355X at the GLM-130B
+// shapes (12288, 36864 and 65536 rows; 12288 and 32768 columns): tall
+// matrices want more row groups per workgroup, short ones more reduction
+// splits (more wavefronts per row), and more token blocks want more row
+// groups per wavefront (each activation operand feeds more MFMAs).
+template <bool GEGLU, bool TILED>
 static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const void *packed,
                                        const void *scales, int64_t n_out, const void *bias, void *y,
-                                       bool geglu, hipStream_t stream)
+                                       hipStream_t stream)
 {
-    if (m <= 16) {
-        if (geglu)
-            launch_decode_small<2, 2, 2, true, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    const int64_t rows = GEGLU ? 2 * n_out : n_out;
+    const int tall = rows >= 49152 ? 2 : rows >= 24576 ? 1 : 0;
+#define W4_DEC(KU, RG, D, MB, MR, NGW)                                                            \
+    launch_decode_e<KU, RG, D, MB, MR, NGW, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, \
+                                                          stream)
+    if constexpr (GEGLU) {
+        // a wavefront always holds gate and value groups: NGW even
+        if (m <= 4)
+            tall == 2 ? W4_DEC(4, 4, 2, 1, 4, 2) : W4_DEC(2, 2, 2, 1, 4, 2);
+        else if (m <= 8)
+            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 2) : W4_DEC(4, 2, 2, 1, 8, 2);
+        else if (m <= 16)
+            tall == 2 ? W4_DEC(4, 4, 2, 1, 16, 2) : W4_DEC(4, 2, 2, 1, 16, 2);
+        else if (m <= 32)
+            W4_DEC(2, 2, 2, 2, 32, 4);
+        else if (m <= 48)
+            W4_DEC(2, 2, 2, 3, 48, 2);
         else
-            launch_decode_small<2, 2, 2, false, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
-        return hipGetLastError();
+            tall == 2 ? W4_DEC(2, 4, 2, 4, 64, 4) : W4_DEC(2, 2, 2, 4, 64, 2);
+    } else {
+        if (m <= 4)
+            tall == 2 ? W4_DEC(4, 4, 2, 1, 4, 1)
+                      : tall ? W4_DEC(2, 2, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
+        else if (m <= 8)
+            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 1) : W4_DEC(4, 2, 2, 1, 8, 1);
+        else if (m <= 16)
+            tall == 2 ? W4_DEC(4, 4, 2, 1, 16, 2)
+                      : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(4, 2, 2, 1, 16, 2);
+        else if (m <= 32)
+            tall == 2 ? W4_DEC(2, 2, 2, 2, 32, 4)
+                      : tall ? W4_DEC(2, 4, 2, 2, 32, 1) : W4_DEC(2, 2, 2, 2, 32, 2);
+        else if (m <= 48)
+            W4_DEC(2, 2, 2, 3, 48, 2);
+        else
+            tall ? W4_DEC(2, 4, 2, 4, 64, 2) : W4_DEC(2, 2, 2, 4, 64, 2);
     }
-    const int mb = (m + 15) / 16;
-#define W4_DECODE_CASE(MBV)                                                                       \
-    case MBV:                                                                                     \
-        if (geglu)                                                                                \
-            launch_decode_mb<MBV, true, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);  \
-        else                                                                                      \
-            launch_decode_mb<MBV, false, TILED>(x, m, k, packed, scales, n_out, bias, y, stream); \
-        break;
-    switch (mb) {
-        W4_DECODE_CASE(2)
-        W4_DECODE_CASE(3)
-        W4_DECODE_CASE(4)
-    default:
-        return hipErrorInvalidValue;
-    }
-#undef W4_DECODE_CASE
+#undef W4_DEC
     return hipGetLastError();
 }
 
@@ -539,9 +382,11 @@ hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, co
                          int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
                          hipStream_t stream)
 {
-    if (tiled)
-        return launch_decode_layout<true>(x, m, k, packed, scales, n_out, bias, y, geglu, stream);
-    return launch_decode_layout<false>(x, m, k, packed, scales, n_out, bias, y, geglu, stream);
+    if (geglu)
+        return tiled ? launch_decode_layout<true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                     : launch_decode_layout<true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+    return tiled ? launch_decode_layout<false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                 : launch_decode_layout<false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
 }
 
 }  // namespace w4a16

@@ -3,8 +3,8 @@
     python -m weight_only_int4_rowwise_amd.profile_run --m 64 --reps 10
 
 Launches the decode QKV linear (36864 x 12288 INT4 row-wise weights,
-rotating over 5 matrices so every launch streams from HBM) `reps` times at
-token count m, then a plain device-to-device copy of exactly 1 GiB (torch
+rotating over 5 matrices so every launch streams from HBM; prepacked or
+row-major layout) `reps` times at token count m, then a plain device-to-device copy of exactly 1 GiB (torch
 copy_) `reps` times.  The copy has a known HBM traffic (1 GiB read, 1 GiB
 written per launch), which calibrates what FETCH_SIZE / WRITE_SIZE report
 per byte on this GPU.
@@ -20,6 +20,7 @@ def main(argv=None):
     ap.add_argument("--m", type=int, default=64)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--layout", choices=("prepacked", "row-major"), default="prepacked")
     a = ap.parse_args(argv)
 
     import torch
@@ -31,15 +32,19 @@ def main(argv=None):
     qs = []
     for i in range(5):
         w = synth.weight(n, k, synth.generator(10 + i, dev), device=dev)
-        qs.append(w4.quantize_rowwise_int4(w))
+        q, s = w4.quantize_rowwise_int4(w)
         del w
+        qs.append((q, s, w4.w4a16_prepack(q)))
     x = synth.activations(a.m, k, synth.generator(0, dev), dev)
     y = torch.empty(a.m, n, dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
-    print(f"decode QKV m={a.m}: {a.reps} launches", flush=True)
+    print(f"decode QKV m={a.m} ({a.layout}): {a.reps} launches", flush=True)
     for r in range(a.reps):
-        q, s = qs[r % 5]
-        w4.w4a16_linear(x, q, s, y_out=y)
+        q, s, qp = qs[r % 5]
+        if a.layout == "prepacked":
+            w4.w4a16_linear_prepacked(x, qp, s, y_out=y)
+        else:
+            w4.w4a16_linear(x, q, s, y_out=y)
     torch.cuda.synchronize()
     src = torch.empty(a.copy_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
