@@ -39,6 +39,11 @@
  *  - Sizes are checked first.  m == 0 or n == 0 (f == 0) is then a valid
  *    empty call: nothing is launched and the pointers are not looked at
  *    (they may be NULL).
+ *  - Size limit of the linears: the activations (2 m k bytes) and the
+ *    packed weight (in its layout) must each be smaller than 2 GiB, since
+ *    the kernels address them with 32-bit buffer offsets; larger calls
+ *    return W4A16_ERR_SHAPE.  The largest GLM-130B weight (the 65536 x
+ *    12288 GeGLU up-projection, 384 MiB packed) is far below it.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -127,12 +132,14 @@ w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k,
  * pages' FasterTransformer port applies ("pre-transposing parameters",
  * paperlayer.ai summary, section B.5), here for gfx950's matrix cores.
  *
- * Same packed bytes and nibble encoding as quantize_rowwise_int4's output,
- * in another order: the weight is cut into tiles of 16 rows x 128 input
+ * Same codes and nibble encoding as quantize_rowwise_int4's output, in
+ * another order: the weight is cut into tiles of 16 rows x 128 input
  * features (1024 bytes); tile (g, t) -- rows [16g, 16g+16), features
  * [128t, 128t+128) -- is stored at byte ((g * ceil(k/128)) + t) * 1024, and
- * inside it the 16 bytes at offset 16 * l (l = 16 j + r, j < 4, r < 16) are
- * packed bytes [64t + 16j, 64t + 16j + 16) of row 16g + r.  Rows past n and
+ * inside it the 16 bytes at offset 16 * l (l = 16 j + r, j < 4, r < 16) hold
+ * packed bytes [64t + 16j, 64t + 16j + 16) of row 16g + r, with the codes
+ * e0..e7 of each 4-byte word stored as the bytes e0|e2<<4, e4|e6<<4,
+ * e1|e3<<4, e5|e7<<4 (the order the dequantizer unpacks).  Rows past n and
  * features past k are zero codes.  Each tile is then one contiguous read
  * in exactly the order the kernels consume it.
  *

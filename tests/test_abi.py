@@ -118,3 +118,22 @@ def test_prepacked_size_and_checks(lib):
     lp = lib.w4a16_linear_prepacked
     assert lp(A, 1, 48, B, C, 16, None, D, None) == _lib.ERR_SHAPE
     assert lp(None, 1, 64, B, C, 16, None, D, None) == _lib.ERR_NULL
+
+
+@pytest.mark.parametrize("fn,geglu", [("w4a16_linear", False), ("w4a16_geglu_linear", True),
+                                      ("w4a16_linear_prepacked", False),
+                                      ("w4a16_geglu_linear_prepacked", True)])
+def test_buffer_size_limit(lib, fn, geglu):
+    """Activations and packed weights must each stay below 2 GiB (32-bit buffer offsets)."""
+    f = getattr(lib, fn)
+    k = 32768
+    m_max = (1 << 31) // (2 * k)                          # 2 m k == 2 GiB exactly
+    assert f(A, m_max, k, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+    assert f(A, m_max - 1, k, B, C, 16, None, MIS, None) == _lib.ERR_ALIGN
+    rows = (1 << 31) // (k // 2)                          # packed weight == 2 GiB exactly
+    n = rows // 2 if geglu else rows
+    assert f(A, 1, k, B, C, n, None, D, None) == _lib.ERR_SHAPE
+    # the GLM-130B FFN up-projection (2 x 32768 rows x 12288) is accepted by the
+    # size check (the call then fails on the fake pointers' alignment)
+    n = 32768 if geglu else 65536
+    assert f(A, 1, 12288, B, C, n, None, MIS, None) == _lib.ERR_ALIGN

@@ -276,7 +276,9 @@ def test_empty_and_rejected_calls():
 # ------------------------------------------------------------ prepacked layout
 
 def _prepack_reference(p_ref: np.ndarray, n: int, k: int) -> np.ndarray:
-    """The prepacked layout written out from its definition (include/w4a16.h)."""
+    """The prepacked layout written out from its definition (include/w4a16.h):
+    1 KB tiles in lane order, each dword's codes e0..e7 stored as bytes
+    e0|e2<<4, e4|e6<<4, e1|e3<<4, e5|e7<<4."""
     ng, kt = -(-n // 16), -(-k // 128)
     out = np.zeros((ng, kt, 64, 16), dtype=np.uint8)
     padded = np.zeros((ng * 16, kt * 64), dtype=np.uint8)
@@ -285,7 +287,13 @@ def _prepack_reference(p_ref: np.ndarray, n: int, k: int) -> np.ndarray:
         r, j = lane % 16, lane // 16
         for t in range(kt):
             out[:, t, lane, :] = padded[r::16, 64 * t + 16 * j: 64 * t + 16 * j + 16]
-    return out.reshape(-1)
+    d = out.reshape(-1, 4)
+    e = np.empty((d.shape[0], 8), dtype=np.uint8)
+    e[:, 0::2] = d & 0xF
+    e[:, 1::2] = d >> 4
+    nib = np.stack([e[:, 0] | (e[:, 2] << 4), e[:, 4] | (e[:, 6] << 4),
+                    e[:, 1] | (e[:, 3] << 4), e[:, 5] | (e[:, 7] << 4)], axis=1)
+    return nib.astype(np.uint8).reshape(-1)
 
 
 @pytest.mark.parametrize("n,k", [(48, 256), (37, 160), (1000, 1120), (16, 128)])

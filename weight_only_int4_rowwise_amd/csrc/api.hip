@@ -28,6 +28,8 @@ thread_local char g_last_error[256] = "";
 // 2048 tokens) fit with room to spare.
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kDecodeMaxM = 64;
+// Activations and weights must each stay below 2 GiB (32-bit buffer offsets).
+constexpr int64_t kMaxBufferBytes = int64_t(1) << 31;
 
 bool aligned16(const void *p)
 {
@@ -48,10 +50,15 @@ w4a16_status from_hip(hipError_t e)
 
 // Sizes first: an empty call (m == 0 or rows == 0) is valid whatever the
 // pointers are (torch hands out NULL for empty tensors).
-w4a16_status check_gemm_shape(int64_t m, int64_t k, int64_t rows)
+w4a16_status check_gemm_shape(int64_t m, int64_t k, int64_t rows, bool tiled)
 {
     if (m < 0 || rows < 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || rows > kMaxDim ||
         k > kMaxDim || m * k > (int64_t(1) << 40) || m * rows > (int64_t(1) << 40))
+        return W4A16_ERR_SHAPE;
+    // the kernels address the activations and the weight with 32-bit
+    // buffer offsets
+    const int64_t wbytes = tiled ? w4a16::prepacked_bytes(rows, k) : rows * (k / 2);
+    if (2 * m * k >= kMaxBufferBytes || wbytes >= kMaxBufferBytes)
         return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
@@ -72,7 +79,7 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
                         void *stream)
 {
     const int64_t rows = geglu ? 2 * n_out : n_out;
-    w4a16_status st = check_gemm_shape(m, k, rows);
+    w4a16_status st = check_gemm_shape(m, k, rows, tiled);
     if (st != W4A16_OK)
         return st;
     if (m == 0 || n_out == 0)

@@ -20,7 +20,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
-// INT4 -> FP16 dequantization of one dword (8 codes) into one MFMA operand.
+// INT4 -> FP16 dequantization of one dword (8 codes) into one MFMA operand
+// holding the 8 codes in their natural order.
 //
 // Flipping bit 3 of a nibble turns the two's-complement code q into the
 // offset-binary u = q + 8 in [1, 15].  Placing u in the mantissa of a
@@ -30,15 +31,20 @@ constexpr int kWave = 64;
 // and one packed f16 subtract of 1032 or 72 returns q exactly.  The flip,
 // the nibble mask and the exponent bits fold into one 3-input bit op:
 //   ((w ^ 0x8888...) & M) | C  ==  (w & M) ^ B,   B = (0x8888... & M) | C
-// since C has no bits inside M.  So 8 codes cost 9 VALU ops: one shift,
-// four v_bitop3_b32, four v_pk_add_f16.  The four packed dwords hold the
-// codes of byte offsets (k0,k4) (k1,k5) (k2,k6) (k3,k7): element e of the
-// operand is code kPerm[e] of the dword.  The other operand is permuted
-// the same way, and since a dot product does not depend on the order of
-// its terms the result is unchanged.
+// since C has no bits inside M.
+//
+// dequant8 reads the prepacked nibble order, in which the dword of codes
+// e0..e7 holds bytes (e0 | e2 << 4), (e4 | e6 << 4), (e1 | e3 << 4),
+// (e5 | e7 << 4): the half pairs (e0,e1) (e2,e3) (e4,e5) (e6,e7) are then
+// the low nibbles of bytes 0 and 2, their high nibbles, and the same for
+// bytes 1 and 3.  9 VALU ops: one shift, four v_bitop3_b32, four
+// v_pk_add_f16.
+//
+// dequant8_rm reads the row-major order of the pages' packing (byte i =
+// e_2i | e_2i+1 << 4): one v_perm_b32 copies byte i into both halves, then
+// its low nibble is e_2i in the low half and its high nibble e_2i+1 in the
+// high half.  12 VALU ops.
 // ---------------------------------------------------------------------------
-__device__ constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-
 __device__ __forceinline__ half2v bits_to_h2(uint32_t v)
 {
     return __builtin_bit_cast(half2v, v);
@@ -51,10 +57,10 @@ __device__ __forceinline__ half8 dequant8(uint32_t packed)
     const half2v hi_bias = {(_Float16)72.0f, (_Float16)72.0f};
     // low nibbles: mask 0x000F000F, exponent 0x6400, flip 0x0008
     // high nibbles: mask 0x00F000F0, exponent 0x5400, flip 0x0080
-    const half2v p0 = bits_to_h2((packed & 0x000F000Fu) ^ 0x64086408u) - lo_bias;   // k0, k4
-    const half2v p1 = bits_to_h2((packed & 0x00F000F0u) ^ 0x54805480u) - hi_bias;   // k1, k5
-    const half2v p2 = bits_to_h2((w8 & 0x000F000Fu) ^ 0x64086408u) - lo_bias;       // k2, k6
-    const half2v p3 = bits_to_h2((w8 & 0x00F000F0u) ^ 0x54805480u) - hi_bias;       // k3, k7
+    const half2v p0 = bits_to_h2((packed & 0x000F000Fu) ^ 0x64086408u) - lo_bias;   // e0, e1
+    const half2v p1 = bits_to_h2((packed & 0x00F000F0u) ^ 0x54805480u) - hi_bias;   // e2, e3
+    const half2v p2 = bits_to_h2((w8 & 0x000F000Fu) ^ 0x64086408u) - lo_bias;       // e4, e5
+    const half2v p3 = bits_to_h2((w8 & 0x00F000F0u) ^ 0x54805480u) - hi_bias;       // e6, e7
     u32x4 r;
     r[0] = __builtin_bit_cast(uint32_t, p0);
     r[1] = __builtin_bit_cast(uint32_t, p1);
@@ -63,16 +69,35 @@ __device__ __forceinline__ half8 dequant8(uint32_t packed)
     return __builtin_bit_cast(half8, r);
 }
 
-// Eight consecutive fp16 activations (as four dwords, natural order) into
-// the operand order kPerm that matches dequant8.
-__device__ __forceinline__ u32x4 permute_x8(u32x4 d)
+__device__ __forceinline__ half8 dequant8_rm(uint32_t packed)
 {
-    u32x4 p;
-    p[0] = (d[0] & 0xFFFFu) | (d[2] << 16);          // x0, x4
-    p[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);      // x1, x5
-    p[2] = (d[1] & 0xFFFFu) | (d[3] << 16);          // x2, x6
-    p[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);      // x3, x7
-    return p;
+    const half2v bias = {(_Float16)1032.0f, (_Float16)72.0f};
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // byte i into bits [7:0] and [23:16], zeros elsewhere (selector 0x0c)
+        const uint32_t sel = 0x0c000c00u | (uint32_t)i | ((uint32_t)i << 16);
+        const uint32_t b = __builtin_amdgcn_perm(0u, packed, sel);
+        const half2v p = bits_to_h2((b & 0x00F0000Fu) ^ 0x54806408u) - bias;
+        r[i] = __builtin_bit_cast(uint32_t, p);
+    }
+    return __builtin_bit_cast(half8, r);
+}
+
+template <bool PREPACKED>
+__device__ __forceinline__ half8 dequant8_of(uint32_t packed)
+{
+    return PREPACKED ? dequant8(packed) : dequant8_rm(packed);
+}
+
+// Row-major packed dword -> the prepacked nibble order read by dequant8.
+__host__ __device__ __forceinline__ uint32_t prepack_nibbles(uint32_t w)
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu;          // e0 e2 e4 e6 in bytes 0..3
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // e1 e3 e5 e7
+    const uint32_t lp = lo | (lo >> 4);           // byte 0 = e0|e2<<4, byte 2 = e4|e6<<4
+    const uint32_t hp = hi | (hi >> 4);
+    return (lp & 0xFFu) | ((lp >> 8) & 0xFF00u) | ((hp & 0xFFu) << 16) | ((hp << 8) & 0xFF000000u);
 }
 
 __device__ __forceinline__ half8 as_half8(u32x4 v)
@@ -124,6 +149,17 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+
+// 16-byte range-checked buffer load written straight to LDS (gfx950 LDS
+// DMA): lane l's 16 bytes land at lds + 16 l, so a wavefront fills 1 KB of
+// consecutive LDS; lds must be the same for all lanes.  Completion is
+// tracked by the vector-memory counter only, so a barrier that publishes
+// the data must be preceded by a wait on that counter.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             (int)off, 0, 0, 0);
 }
 
 // Byte offset of the 16 packed bytes (32 codes, reduction indices

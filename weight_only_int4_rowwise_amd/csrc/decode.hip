@@ -8,8 +8,9 @@
 // to stream the weights from HBM once at full bandwidth (one kernel
 // template below, shaped per token count):
 //
-//  * Codes become exact fp16 integers in registers (dequant8: 1.25 VALU ops
-//    per code) and feed v_mfma_f32_16x16x32_f16 with 16 weight rows as the
+//  * Codes become exact fp16 integers in registers (dequant8: 9 VALU ops
+//    per 8 codes of the prepacked layout, 12 for the row-major one) and
+//    feed v_mfma_f32_16x16x32_f16 with 16 weight rows as the
 //    A operand and up to 16 tokens per MFMA as the B operand, fp32
 //    accumulation.  Padding m up to 16 costs idle MFMA slots, not bytes.
 //  * Every load is an unconditional range-checked buffer load (padding
@@ -44,14 +45,13 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 //
 // The activation chunks of a round (KS chunks, MR x 128 KU fp16 each; MR =
 // m rounded up to 4, 8 or 16 for one block, 16 MB otherwise) are loaded
-// once per workgroup, permuted into the dequant8 operand order and
-// double-buffered in LDS, one barrier per round; the RG wavefronts that
+// once per workgroup and double-buffered in LDS, one barrier per round; the RG wavefronts that
 // work on the same chunk share it.  Each round's activation loads are
 // issued before its weight loads: vector loads retire in order, so waiting
 // for the activations does not wait for the weights.  Partial sums of the
 // KS wavefronts of a row set meet in LDS in a fixed order.
 //
-// The dequantization is the bulk of the VALU work (9 ops per 8 codes), so
+// The dequantization is the bulk of the VALU work, so
 // everything else is kept off the VALU: every lane's load offset is a
 // per-lane constant plus a wave-uniform step.  Rows past the end are
 // clamped to the last row and tokens past m to token m - 1 (they only feed
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
         for (int i = 0; i < XP; ++i) {
             const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
             const int q = idx / RP;
-            *reinterpret_cast<u32x4 *>(&xs[buf][q / MR][q % MR][8 * (idx % RP)]) = permute_x8(xr[i]);
+            *reinterpret_cast<u32x4 *>(&xs[buf][q / MR][q % MR][8 * (idx % RP)]) = xr[i];
         }
     };
     const int brow = r16 < MR ? r16 : MR - 1;          // MFMA columns past MR repeat row MR - 1
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
                         &xs[buf][kp][16 * b + brow][32 * g + 128 * p + 8 * t]));
 #pragma unroll
                 for (int j = 0; j < NGW; ++j) {
-                    const half8 a = dequant8(wd[j][p][t]);
+                    const half8 a = dequant8_of<TILED>(wd[j][p][t]);
 #pragma unroll
                     for (int b = 0; b < MB; ++b)
                         acc[j][b][t % CH] = mfma16x16x32(a, bx[b], acc[j][b][t % CH]);

@@ -6,33 +6,38 @@
 // y[i][r] = fp16(s[r] * sum_c x[i][c] * q[r][c] + bias[r]), fp32 accumulation,
 // optional fused GeGLU (paper card "Hyperparameters"; paperlayer.ai B.3).
 //
-// Tiling.  A 256-thread workgroup computes a 128 (weight rows) x 128
-// (tokens) output tile over 128-wide reduction steps; wave w owns the
-// 64 x 64 quadrant (w & 1, w >> 1), i.e. 4 x 4 MFMA 16x16 tiles.
-//  * Activations: the 128 x 128 fp16 step tile is copied global -> LDS once
-//    per workgroup (permuted into the operand order of dequant8 as it is
-//    written), double-buffered so the next step's copy overlaps this step's
-//    MFMAs.  Rows are padded to 272 bytes so the 16 lanes that read one
-//    operand column hit distinct LDS banks.
+// Tiling.  A 256-thread workgroup computes a (4 x 16 WN weight rows) x
+// (16 WT tokens) output tile over 128-wide reduction steps.  The four
+// wavefronts split the rows: wave w owns WN groups of 16 rows and all WT
+// token blocks, i.e. WN x WT MFMA 16x16 tiles.  Dequantizing the weights
+// is the main VALU cost, so each dequantized A operand feeds WT MFMAs and
+// each activation B operand read from LDS feeds WN MFMAs.
+//  * Activations: the (16 WT) x 128 fp16 step tile goes global -> LDS by
+//    LDS DMA (buffer loads that write LDS directly: no registers, no VALU),
+//    double-buffered so the next step's copy overlaps this step's MFMAs.
+//    Each token row is 256 bytes = 16 pieces of 16 bytes; piece p of row r
+//    is stored at piece p ^ (r mod 16), so the 16 lanes that read one
+//    operand column (16 rows, one piece) hit 16 distinct bank groups.
 //  * Weights: each lane loads its 16 packed bytes per row group straight
 //    into registers (one dwordx4, prefetched a step ahead) and dequantizes
 //    them into the MFMA A operand: the fp16 weight tile never exists in
 //    memory.  The scale is applied once per output in the epilogue.
-//  * All loads are unconditional range-checked buffer loads and the step
-//    loop is unrolled twice over two weight register sets, so the next
-//    step's loads stay in flight while this step's MFMAs run.
+//  * All loads are unconditional range-checked buffer loads at a per-lane
+//    constant offset plus a wave-uniform step.  Rows and tokens past the
+//    end are clamped to the last one (their results are never stored) and
+//    steps past the end read zeros.  The step loop is unrolled twice over
+//    two weight register sets, so no register copy forces a load to retire
+//    early.
 #include "common.hpp"
 
 namespace w4a16 {
 
-constexpr int kPBN = 128;           // weight rows per tile
-constexpr int kPBM = 128;           // tokens per tile
-constexpr int kPBK = 128;           // reduction step
-constexpr int kPLd = kPBK + 8;      // LDS row stride in halves (272 bytes)
+constexpr int kPBK = 128;                 // reduction step
+constexpr int kPRowBytes = 2 * kPBK;      // bytes of one token row per step
 constexpr int kPThreads = 256;
 
-template <bool GEGLU, bool TILED>
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__restrict__ x,
+template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED>
+__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *__restrict__ x,
                                                             int64_t m, int64_t k,
                                                             const uint8_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
@@ -41,175 +46,200 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(const uint16_t *__re
                                                             uint16_t *__restrict__ y,
                                                             int tiles_m)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kPBM * kPLd];
+    static_assert(!GEGLU || WN % 2 == 0, "GeGLU pairs gate and value row groups");
+    constexpr int BM = 16 * WT;                       // tokens per tile
+    constexpr int NO = GEGLU ? WN / 2 : WN;           // output row groups per wave
+    constexpr int kStepBytes = BM * kPRowBytes;       // activation tile of one step
+    constexpr int XC = kStepBytes / (4 * 1024);       // 1 KB DMA loads per wave per step
+    static_assert(XC * 4 * 1024 == kStepBytes, "activation tile must split into 1 KB loads");
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kStepBytes];
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    const int wn = wave & 1, wm = wave >> 1;
     const int r16 = lane % 16;
     const int g = lane / 16;
 
     const int tile_m = blockIdx.x % tiles_m;
     const int64_t tile_n = blockIdx.x / tiles_m;
-    const int64_t m0 = (int64_t)tile_m * kPBM;
-    constexpr int kOutPerTile = GEGLU ? kPBN / 2 : kPBN;
-    const int64_t o0 = tile_n * kOutPerTile;
+    const int64_t m0 = (int64_t)tile_m * BM;
+    const int64_t o0 = (tile_n * 4 + wave) * (16 * NO);   // first output of this wave
     const int64_t kb = k / 2;
-    const int64_t kt = (k + 127) / 128;   // tiles per row group (prepacked layout)
-
-    // base offset of the weight row of this lane in group j (4 groups of 16 per wave)
-    uint32_t wbase[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int64_t r;
-        bool ok;
-        if (GEGLU) {
-            const int64_t f = o0 + 32 * wn + 16 * (j % 2) + r16;
-            ok = f < n_out;
-            r = (j < 2) ? f : n_out + f;
-        } else {
-            r = o0 + 64 * wn + 16 * j + r16;
-            ok = r < n_out;
-        }
-        wbase[j] = row_base_off<TILED>(ok ? r : -1, kb, kt, lane);
-    }
-    const uint32_t k32 = (uint32_t)k;
-
-    float4v acc[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            acc[j][b] = float4v{0.f, 0.f, 0.f, 0.f};
-
+    const int64_t kt = (k + 127) / 128;
     const int64_t nsteps = (k + kPBK - 1) / kPBK;
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m * k * 2);
+    const uint32_t k32 = (uint32_t)k;
 
-    // activation copy: 128 rows x 16 pieces of 16 bytes; thread handles 8
-    // pieces.  Issued before the same stage's weight loads: loads retire in
-    // order, so storing them to LDS does not wait for the weights.
-    u32x4 xr[8];
-    uint32_t xrow[8];
+    // per-lane constant part of the weight offsets; row group j is output
+    // group j % NO, and for GeGLU j >= NO is the value partner of gate j - NO
+    uint32_t wbase[WN];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = threadIdx.x + kPThreads * i;
-        const int64_t mi = m0 + c / 16;
-        xrow[i] = mi < m ? (uint32_t)((mi * k + 8 * (c % 16)) * 2) : kOutOfRange;
+    for (int j = 0; j < WN; ++j) {
+        int64_t o = o0 + 16 * (j % NO) + r16;
+        if (o >= n_out)
+            o = n_out - 1;
+        const int64_t row = j >= NO ? n_out + o : o;
+        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 + 16 * lane)
+                         : (uint32_t)(row * kb + 16 * g);
     }
-    auto load_x = [&](int64_t s) {
+    // DMA load i of this wave fills LDS bytes [1024 c, 1024 c + 1024) of the
+    // step tile, c = XC wave + i: lane l writes token row 4 c + l / 16 at
+    // stored piece l % 16, i.e. it fetches logical piece (l % 16) ^ (row % 16)
+    uint32_t xbase[XC], xcol[XC];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = threadIdx.x + kPThreads * i;
-            const uint32_t kk = (uint32_t)s * kPBK + 8 * (c % 16);
-            xr[i] = buf_load16(xrs, kk < k32 ? xrow[i] + 2 * (uint32_t)s * kPBK : kOutOfRange);
+    for (int i = 0; i < XC; ++i) {
+        const int row = 4 * (XC * wave + i) + lane / 16;
+        const int piece = (lane % 16) ^ (row % 16);
+        int64_t mi = m0 + row;
+        if (mi >= m)
+            mi = m - 1;
+        xcol[i] = 8 * piece;
+        xbase[i] = (uint32_t)(mi * k * 2 + 16 * piece);
+    }
+    // LDS read offsets of this lane's B operand pieces: token row r16 of
+    // each block, logical piece 4 g + t
+    uint32_t rdoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        rdoff[t] = r16 * kPRowBytes + 16 * ((4 * g + t) ^ r16);
+
+    float4v acc[WN][WT];
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int b = 0; b < WT; ++b)
+            acc[j][b] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // Offsets below 2^31 plus kOutOfRange stay below 2^32 and out of range,
+    // so a step past the end reads zeros.
+    auto load_x = [&](int64_t s, int buf) {
+        const uint32_t step = s < nsteps ? (uint32_t)s * kPRowBytes : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            uint32_t off = xbase[i] + step;
+            if (!EVEN && (uint32_t)s * kPBK + xcol[i] >= k32)
+                off = kOutOfRange;
+            buf_load16_lds(xrs, off, &xs[buf][1024 * (XC * wave + i)]);
         }
     };
-    auto store_x = [&](int buf) {
+    auto load_w = [&](int64_t s, u32x4(&wd)[WN]) {
+        const uint32_t u = (uint32_t)s * kPBK;
+        const uint32_t step = s < nsteps ? (TILED ? (uint32_t)s * 1024u : u / 2) : kOutOfRange;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = threadIdx.x + kPThreads * i;
-            const int rr = c / 16;
-            *reinterpret_cast<u32x4 *>(&xs[buf][rr * kPLd + 8 * (c % 16)]) = permute_x8(xr[i]);
+        for (int j = 0; j < WN; ++j) {
+            uint32_t off = wbase[j] + step;
+            if (!EVEN && !TILED && u + 32 * g >= k32)
+                off = kOutOfRange;
+            wd[j] = buf_load16_stream(wrs, off);
         }
     };
-    auto load_w = [&](int64_t s, u32x4(&wd)[4]) {
-        const uint32_t kc = (uint32_t)s * kPBK + 32 * g;
-        const uint32_t step = piece_step_off<TILED>(kc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wd[j] = buf_load16_stream(wrs, kc < k32 ? wbase[j] + step : kOutOfRange);
-    };
-    auto compute = [&](int buf, const u32x4(&wd)[4]) {
+    // MFMA t of a step covers, for lane group g, reduction indices
+    // 32 g + 8 t .. + 7 of the step on both operands.  The WN dequantized
+    // A operands stay live while the B operands stream through.
+    auto compute = [&](int buf, const u32x4(&wd)[WN]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            half8 bx[4];
+            half8 a[WN];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int rr = 64 * wm + 16 * b + r16;
-                bx[b] = as_half8(*reinterpret_cast<const u32x4 *>(&xs[buf][rr * kPLd + 32 * g + 8 * t]));
-            }
+            for (int j = 0; j < WN; ++j)
+                a[j] = dequant8_of<TILED>(wd[j][t]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const half8 a = dequant8(wd[j][t]);
+            for (int b = 0; b < WT; ++b) {
+                const half8 bx = as_half8(*reinterpret_cast<const u32x4 *>(
+                    &xs[buf][rdoff[t] + 16 * kPRowBytes * b]));
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[j][b] = mfma16x16x32(a, bx[b], acc[j][b]);
+                for (int j = 0; j < WN; ++j)
+                    acc[j][b] = mfma16x16x32(a[j], bx, acc[j][b]);
             }
         }
+    };
+    // every wave waits for its own DMA writes before the barrier that
+    // hands the buffer to the other waves
+    auto publish = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
     };
 
     // two register sets for the weights, used alternately (the loop is
     // unrolled twice so no set is ever copied)
-    u32x4 wa[4], wb[4];
-    load_x(0);
+    u32x4 wa[WN], wb[WN];
+    load_x(0, 0);
     load_w(0, wa);
-    store_x(0);
-    __syncthreads();
+    publish();
     for (int64_t s = 0;;) {
-        load_x(s + 1);
+        load_x(s + 1, 1);
         load_w(s + 1, wb);
         compute(0, wa);
-        store_x(1);
-        __syncthreads();
+        publish();
         if (++s >= nsteps)
             break;
-        load_x(s + 1);
+        load_x(s + 1, 0);
         load_w(s + 1, wa);
         compute(1, wb);
-        store_x(0);
-        __syncthreads();
+        publish();
         if (++s >= nsteps)
             break;
     }
 
-    // epilogue: lane holds D[4 g + i][r16] of tile (j, b): weight row 4 g + i, token r16
+    // epilogue: lane holds D[4 g + i][r16] of tile (j, b), i.e. outputs
+    // 16 j + 4 g + i of the wave for token 16 b + r16: four consecutive
+    // outputs, stored as one 8-byte write when all are in range and aligned
+    const bool vec = (n_out % 4) == 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int64_t mi = m0 + 64 * wm + 16 * b + r16;
+    for (int b = 0; b < WT; ++b) {
+        const int64_t mi = m0 + 16 * b + r16;
         if (mi >= m)
             continue;
-        if (GEGLU) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NO; ++j) {
+            const int64_t ob = o0 + 16 * j + 4 * g;
+            if (ob >= n_out)
+                continue;
+            uint16_t h[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t f = o0 + 32 * wn + 16 * j + 4 * g + i;
-                    if (f >= n_out)
-                        continue;
-                    float a = acc[j][b][i] * half_bits_to_float(scales[f]);
-                    float bv = acc[j + 2][b][i] * half_bits_to_float(scales[n_out + f]);
+            for (int i = 0; i < 4; ++i) {
+                const int64_t o = ob + i < n_out ? ob + i : n_out - 1;
+                float v;
+                if (GEGLU) {
+                    float a = acc[j][b][i] * half_bits_to_float(scales[o]);
+                    float bv = acc[j + NO][b][i] * half_bits_to_float(scales[n_out + o]);
                     if (bias) {
-                        a += half_bits_to_float(bias[f]);
-                        bv += half_bits_to_float(bias[n_out + f]);
+                        a += half_bits_to_float(bias[o]);
+                        bv += half_bits_to_float(bias[n_out + o]);
                     }
-                    y[mi * n_out + f] = float_to_half_bits(gelu_erf(a) * bv);
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t n = o0 + 64 * wn + 16 * j + 4 * g + i;
-                    if (n >= n_out)
-                        continue;
-                    float v = acc[j][b][i] * half_bits_to_float(scales[n]);
+                    v = gelu_erf(a) * bv;
+                } else {
+                    v = acc[j][b][i] * half_bits_to_float(scales[o]);
                     if (bias)
-                        v += half_bits_to_float(bias[n]);
-                    y[mi * n_out + n] = float_to_half_bits(v);
+                        v += half_bits_to_float(bias[o]);
                 }
+                h[i] = float_to_half_bits(v);
+            }
+            uint16_t *dst = y + mi * n_out + ob;
+            if (vec && ob + 3 < n_out) {
+                uint2 pk;
+                pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                *reinterpret_cast<uint2 *>(dst) = pk;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (ob + i < n_out)
+                        dst[i] = h[i];
+            }
         }
     }
 }
 
-hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
-                          const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          bool tiled, hipStream_t stream)
+template <int WN, int WT, bool GEGLU, bool TILED>
+static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const void *packed,
+                                   const void *scales, int64_t n_out, const void *bias, void *y,
+                                   hipStream_t stream)
 {
-    const int64_t out_per = geglu ? kPBN / 2 : kPBN;
+    constexpr int out_per = 4 * 16 * (GEGLU ? WN / 2 : WN);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
-    const int64_t tiles_m = (m + kPBM - 1) / kPBM;
+    const int64_t tiles_m = (m + 16 * WT - 1) / (16 * WT);
     const int64_t grid = tiles_n * tiles_m;
     if (grid > 0x7FFFFFFF)
         return hipErrorInvalidValue;
@@ -218,19 +248,26 @@ hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packe
     const uint16_t *sp = static_cast<const uint16_t *>(scales);
     const uint16_t *bp = static_cast<const uint16_t *>(bias);
     uint16_t *yp = static_cast<uint16_t *>(y);
-#define W4_PREFILL(G, T)                                                                          \
-    hipLaunchKernelGGL((prefill_kernel<G, T>), dim3((unsigned)grid), dim3(kPThreads), 0, stream, xp, \
-                       m, k, pp, sp, n_out, bp, yp, (int)tiles_m)
-    if (geglu && tiled)
-        W4_PREFILL(true, true);
-    else if (geglu)
-        W4_PREFILL(true, false);
-    else if (tiled)
-        W4_PREFILL(false, true);
+#define W4_PREFILL(EV)                                                                            \
+    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED>), dim3((unsigned)grid),          \
+                       dim3(kPThreads), 0, stream, xp, m, k, pp, sp, n_out, bp, yp, (int)tiles_m)
+    if (k % kPBK == 0)
+        W4_PREFILL(true);
     else
-        W4_PREFILL(false, false);
+        W4_PREFILL(false);
 #undef W4_PREFILL
     return hipGetLastError();
+}
+
+hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
+                          const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
+                          bool tiled, hipStream_t stream)
+{
+    if (geglu)
+        return tiled ? launch_prefill_t<4, 8, true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                     : launch_prefill_t<4, 8, true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+    return tiled ? launch_prefill_t<4, 8, false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                 : launch_prefill_t<4, 8, false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
 }
 
 }  // namespace w4a16

@@ -5,8 +5,10 @@
 // weight rows [16 g, 16 g + 16) and reduction indices [128 t, 128 t + 128):
 // 1024 bytes, stored at ((g * ceil(k/128)) + t) * 1024, laid out in the
 // order the MFMA A operand is loaded: 16 bytes per lane, lane l = 16 j + r
-// holding row 16 g + r, packed bytes [64 t + 16 j, +16) of that row.  Rows
-// past n and indices past k are zero codes.  Same bytes, same nibble
+// holding row 16 g + r, packed bytes [64 t + 16 j, +16) of that row, with
+// the nibbles of each dword reordered for dequant8 (codes e0..e7 of the
+// dword as bytes e0|e2<<4, e4|e6<<4, e1|e3<<4, e5|e7<<4).  Rows past n and
+// indices past k are zero codes.  Same codes, same two's-complement nibble
 // encoding: only their order changes, so every 1 KB tile is one contiguous
 // read for a wavefront.
 #include "common.hpp"
@@ -28,8 +30,12 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict_
     const int64_t row = 16 * grp + lane % 16;
     const int64_t byte = 64 * t + 16 * (lane / 16);
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (row < n && byte < k / 2)
+    if (row < n && byte < k / 2) {
         v = load16(src + row * (k / 2) + byte);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = prepack_nibbles(v[i]);
+    }
     *reinterpret_cast<u32x4 *>(dst + idx * 16) = v;
 }
 
