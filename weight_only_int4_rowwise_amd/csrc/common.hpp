@@ -151,6 +151,13 @@ __device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uin
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maximum).
+constexpr int vmcnt_imm(int n)
+{
+    return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70;
+}
+
 // 16-byte range-checked buffer load written straight to LDS (gfx950 LDS
 // DMA): lane l's 16 bytes land at lds + 16 l, so a wavefront fills 1 KB of
 // consecutive LDS; lds must be the same for all lanes.  Completion is

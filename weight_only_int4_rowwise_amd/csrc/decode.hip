@@ -208,7 +208,9 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     // Ring of D weight register sets: round r uses set r % D, loaded D - 1
     // rounds earlier.  The round loop is unrolled D times so every set has
     // a fixed register name (no copies, which would force the loads to
-    // retire early).
+    // retire early).  Scheduling barriers keep each round's loads at its
+    // top, activations first: left alone, the compiler sinks them towards
+    // their first use and the prefetch distance collapses.
     u32x4 wr[D][NGW][KU];
     load_x(0);
 #pragma unroll
@@ -223,7 +225,9 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
             if (r >= rounds)
                 break;
             load_x(r + 1);
+            __builtin_amdgcn_sched_barrier(0);
             load_w(r + D - 1, wr[(i + D - 1) % D]);
+            __builtin_amdgcn_sched_barrier(0);
             compute(i & 1, wr[i]);
             store_x((i & 1) ^ 1);
             __syncthreads();

@@ -19,7 +19,9 @@
 //    is stored at piece p ^ (r mod 16), so the 16 lanes that read one
 //    operand column (16 rows, one piece) hit 16 distinct bank groups.
 //  * Weights: each lane loads its 16 packed bytes per row group straight
-//    into registers (one dwordx4, prefetched a step ahead) and dequantizes
+//    into registers (one dwordx4, prefetched a step ahead, through the
+//    caches: the token tiles of one row block run side by side and share
+//    it) and dequantizes
 //    them into the MFMA A operand: the fp16 weight tile never exists in
 //    memory.  The scale is applied once per output in the epilogue.
 //  * All loads are unconditional range-checked buffer loads at a per-lane
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
             uint32_t off = wbase[j] + step;
             if (!EVEN && !TILED && u + 32 * g >= k32)
                 off = kOutOfRange;
-            wd[j] = buf_load16_stream(wrs, off);
+            wd[j] = buf_load16(wrs, off);
         }
     };
     // MFMA t of a step covers, for lane group g, reduction indices
@@ -154,28 +156,41 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
             }
         }
     };
-    // every wave waits for its own DMA writes before the barrier that
-    // hands the buffer to the other waves
+    // Each step issues its activation DMA, then its WN weight loads, kept
+    // in that order and at the top of the step by scheduling barriers (the
+    // compiler would otherwise sink the weight loads to the end of the
+    // step, next to their first use, and expose their whole latency).
+    // Loads retire in order, so waiting until at most WN are outstanding
+    // means this wave's DMA writes have landed; the barrier then hands the
+    // buffer to the other waves while the weight loads stay in flight.
+    // The fences order only LDS accesses around the barrier.
     auto publish = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WN));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
     // two register sets for the weights, used alternately (the loop is
     // unrolled twice so no set is ever copied)
     u32x4 wa[WN], wb[WN];
     load_x(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(0, wa);
     publish();
     for (int64_t s = 0;;) {
         load_x(s + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         load_w(s + 1, wb);
+        __builtin_amdgcn_sched_barrier(0);
         compute(0, wa);
         publish();
         if (++s >= nsteps)
             break;
         load_x(s + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
         load_w(s + 1, wa);
+        __builtin_amdgcn_sched_barrier(0);
         compute(1, wb);
         publish();
         if (++s >= nsteps)
