@@ -363,12 +363,11 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
             tall == 2 ? W4_DEC(2, 4, 2, 4, 64, 4) : W4_DEC(2, 2, 2, 4, 64, 2);
     } else {
         if (m <= 4)
-            tall == 2 ? W4_DEC(4, 4, 2, 1, 4, 1)
-                      : tall ? W4_DEC(2, 2, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
+            tall == 2 ? W4_DEC(2, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
         else if (m <= 8)
-            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 1) : W4_DEC(4, 2, 2, 1, 8, 1);
+            tall ? W4_DEC(2, 4, 2, 1, 8, 1) : W4_DEC(4, 2, 2, 1, 8, 1);
         else if (m <= 16)
-            tall == 2 ? W4_DEC(4, 4, 2, 1, 16, 2)
+            tall == 2 ? W4_DEC(2, 4, 2, 1, 16, 2)
                       : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(4, 2, 2, 1, 16, 2);
         else if (m <= 32)
             tall == 2 ? W4_DEC(2, 2, 2, 2, 32, 4)
