@@ -88,7 +88,13 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     static_assert(D % 2 == 0, "the LDS double buffer alternates with the round parity");
     constexpr int CH = MB == 1 ? 2 : 1;       // independent accumulator chains per (group, block)
     constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;   // outputs per wave
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][KS][MR][LD];
+    // LDS: the double-buffered activation chunks during the loop, the
+    // partial sums of K-parts 1..KS-1 after it (one buffer, two uses)
+    constexpr int kSlot = NGW * MB * kWave * 4;            // partial-sum floats per wave
+    constexpr int kXBytes = 2 * KS * MR * LD * 2;
+    constexpr int kRedBytes = (KS - 1) * RG * kSlot * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kXBytes > kRedBytes ? kXBytes : kRedBytes];
+    auto &xs = *reinterpret_cast<uint16_t(*)[2][KS][MR][LD]>(lds);
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -243,10 +249,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
 
     if (KS > 1) {
         // partial sums of K-parts 1..KS-1 -> LDS; K-part 0 adds them in order
-        constexpr int kSlot = NGW * MB * kWave * 4;   // floats per wave
-        static_assert(sizeof(xs) >= (KS - 1) * RG * kSlot * sizeof(float),
-                      "reduction slots reuse the activation buffer");
-        float *red = reinterpret_cast<float *>(&xs[0][0][0][0]);
+        float *red = reinterpret_cast<float *>(lds);
         if (kp > 0) {
 #pragma unroll
             for (int j = 0; j < NGW; ++j)
@@ -365,10 +368,11 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
         if (m <= 4)
             tall == 2 ? W4_DEC(2, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
         else if (m <= 8)
-            tall ? W4_DEC(2, 4, 2, 1, 8, 1) : W4_DEC(4, 2, 2, 1, 8, 1);
+            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 1)
+                      : tall ? W4_DEC(1, 1, 2, 1, 8, 3) : W4_DEC(2, 1, 2, 1, 8, 3);
         else if (m <= 16)
             tall == 2 ? W4_DEC(2, 4, 2, 1, 16, 2)
-                      : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(4, 2, 2, 1, 16, 2);
+                      : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(2, 1, 2, 1, 16, 3);
         else if (m <= 32)
             tall == 2 ? W4_DEC(2, 2, 2, 2, 32, 4)
                       : tall ? W4_DEC(2, 4, 2, 2, 32, 1) : W4_DEC(2, 2, 2, 2, 32, 2);
