@@ -179,12 +179,9 @@ def main(argv=None):
             tr = json.load(fh)
         if tr.get("csrc_hash") == csrc_hash() and str(dom) in tr.get("bytes_per_launch", {}):
             traffic = tr["bytes_per_launch"][str(dom)]
-    # the library runs the skinny kernel for this shape (2304 groups of 16
-    # rows) at 32 < M <= 64 and the decode kernel below
-    kname = "skinny_kernel (9 row groups per workgroup)" if dom > 32 else "decode_kernel"
     roofline = {
         "bound": "hbm",
-        "kernel": f"{kname}, M={dom} ({mb} token block{'s' if mb > 1 else ''}), prepacked "
+        "kernel": f"decode_kernel, M={dom} ({mb} token block{'s' if mb > 1 else ''}), prepacked "
                   "QKV 36864x12288",
         "achieved": per_m[dom]["GBs"],
         "peak": HBM_PEAK_GBS,

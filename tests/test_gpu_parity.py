@@ -213,50 +213,51 @@ def test_geglu_fused_matches_unfused_halves():
     assert torch.all((fused - unfused).abs() <= tol)
 
 
-# --------------------------------------- skinny GEMM (tall, 32 < m <= 64)
-# Weights with 9 x 256 or 16 x 256 groups of 16 rows (GeGLU: 8 x 256 feature
-# groups) take the skinny kernel at 32 < m <= 64; rows and k are ragged here.
+# ---------------------------------------- tall weights at 32 < m <= 64
+# QKV-, FFN-up- and GeGLU-shaped weights (36864 / 65536 rows, 2 x 32768)
+# take their own decode launch shapes at 32 < m <= 64 (several row groups
+# per wavefront, K split over the workgroup); rows and k are ragged here.
 
 @pytest.mark.parametrize("m,n,k", [(33, 36860, 160), (48, 36864, 256), (49, 36850, 96),
                                    (64, 36864, 160), (40, 65530, 96), (64, 65536, 128)])
-def test_skinny_shapes(m, n, k):
+def test_tall_decode_shapes(m, n, k):
     g = synth.generator(1400 + m + n)
     w = synth.weight(n, k, g, "t4")
     x = synth.activations(m, k, g)
     bias = synth.normal_fp16((n,), 0.5, g)
-    q, s, p_ref, s_ref = quantize_both(w, f"skinny {m}x{n}x{k}")
-    check_linear(x, q, s, p_ref, s_ref, f"skinny {m}x{n}x{k}")
-    check_linear(x, q, s, p_ref, s_ref, f"skinny {m}x{n}x{k} bias", bias)
-    announce("skinny prepacked", m, n, k)
+    q, s, p_ref, s_ref = quantize_both(w, f"tall {m}x{n}x{k}")
+    check_linear(x, q, s, p_ref, s_ref, f"tall {m}x{n}x{k}")
+    check_linear(x, q, s, p_ref, s_ref, f"tall {m}x{n}x{k} bias", bias)
+    announce("tall prepacked", m, n, k)
     xd, bd = x.to(DEV), bias.to(DEV)
     y0 = w4.w4a16_linear(xd, q, s, bd)
     y1 = w4.w4a16_linear_prepacked(xd, w4.w4a16_prepack(q), s, bd)
     torch.cuda.synchronize()
-    assert_bits_equal(bits(y1), bits(y0), f"skinny prepacked vs row-major {m}x{n}x{k}")
+    assert_bits_equal(bits(y1), bits(y0), f"tall prepacked vs row-major {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m", [37, 64])
-def test_skinny_one_hot_and_pow2_bit_exact(m):
+def test_tall_decode_one_hot_and_pow2_bit_exact(m):
     _one_hot_case(m, 36864, 256, 1500 + m)
     _pow2_case(m, 36864, 256, 1600 + m)
 
 
 @pytest.mark.parametrize("m,f,k", [(36, 32768, 160), (64, 32760, 96), (64, 32768, 128)])
-def test_skinny_geglu(m, f, k):
+def test_tall_decode_geglu(m, f, k):
     g = synth.generator(1700 + m + f)
     w = synth.weight(2 * f, k, g, "t4")
     x = synth.activations(m, k, g)
-    q, s, p_ref, s_ref = quantize_both(w, f"skinny geglu f={f} k={k}")
-    check_geglu(x, q, s, p_ref, s_ref, f"skinny geglu {m}x{f}x{k}")
+    q, s, p_ref, s_ref = quantize_both(w, f"tall geglu f={f} k={k}")
+    check_geglu(x, q, s, p_ref, s_ref, f"tall geglu {m}x{f}x{k}")
     bias = synth.normal_fp16((2 * f,), 0.5, g)
-    check_geglu(x, q, s, p_ref, s_ref, f"skinny geglu {m}x{f}x{k} bias", bias)
+    check_geglu(x, q, s, p_ref, s_ref, f"tall geglu {m}x{f}x{k} bias", bias)
     if f % 16 == 0:
-        announce("skinny geglu prepacked", m, f, k)
+        announce("tall geglu prepacked", m, f, k)
         xd = x.to(DEV)
         y0 = w4.w4a16_geglu_linear(xd, q, s)
         y1 = w4.w4a16_geglu_linear_prepacked(xd, w4.w4a16_prepack(q), s)
         torch.cuda.synchronize()
-        assert_bits_equal(bits(y1), bits(y0), f"skinny geglu prepacked vs row-major {m}x{f}x{k}")
+        assert_bits_equal(bits(y1), bits(y0), f"tall geglu prepacked vs row-major {m}x{f}x{k}")
 
 
 # ----------------------------------------------------------- prefill GEMM

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "skinny.hip", "prefill.hip", "prepack.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "prefill.hip", "prepack.hip"]
 ARCH = "gfx950"
 
 

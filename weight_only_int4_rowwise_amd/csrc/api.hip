@@ -12,9 +12,6 @@ hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, vo
 hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
                          int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
                          hipStream_t stream);
-hipError_t launch_skinny(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
-                         hipStream_t stream);
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
                           bool tiled, hipStream_t stream);
@@ -92,13 +89,8 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
         return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (m <= kDecodeMaxM) {
-        // tall weights at 32 < m <= 64 have a faster kernel; any other
-        // shape reports hipErrorNotSupported before launching anything
-        e = w4a16::launch_skinny(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
-        if (e == hipErrorNotSupported)
-            e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
-    }
+    if (m <= kDecodeMaxM)
+        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
     else
         e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, hs);
     return from_hip(e);

@@ -361,9 +361,9 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
         else if (m <= 32)
             W4_DEC(2, 2, 2, 2, 32, 4);
         else if (m <= 48)
-            W4_DEC(2, 2, 2, 3, 48, 2);
+            W4_DEC(1, 2, 2, 3, 48, 4);
         else
-            tall == 2 ? W4_DEC(2, 4, 2, 4, 64, 4) : W4_DEC(2, 2, 2, 4, 64, 2);
+            tall == 2 ? W4_DEC(1, 2, 2, 4, 64, 4) : W4_DEC(2, 2, 2, 4, 64, 2);
     } else {
         if (m <= 4)
             tall == 2 ? W4_DEC(2, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
@@ -374,12 +374,14 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
             tall == 2 ? W4_DEC(2, 4, 2, 1, 16, 2)
                       : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(2, 1, 2, 1, 16, 3);
         else if (m <= 32)
-            tall == 2 ? W4_DEC(2, 2, 2, 2, 32, 4)
-                      : tall ? W4_DEC(2, 4, 2, 2, 32, 1) : W4_DEC(2, 2, 2, 2, 32, 2);
+            tall == 2 ? W4_DEC(2, 4, 2, 2, 32, 2)
+                      : tall ? W4_DEC(1, 2, 2, 2, 32, 3) : W4_DEC(2, 1, 2, 2, 32, 3);
         else if (m <= 48)
-            W4_DEC(2, 2, 2, 3, 48, 2);
+            tall == 2 ? W4_DEC(1, 2, 2, 3, 48, 4)
+                      : tall ? W4_DEC(1, 2, 2, 3, 48, 3) : W4_DEC(1, 1, 2, 3, 48, 3);
         else
-            tall ? W4_DEC(2, 4, 2, 4, 64, 2) : W4_DEC(2, 2, 2, 4, 64, 2);
+            tall == 2 ? W4_DEC(1, 2, 2, 4, 64, 4)
+                      : tall ? W4_DEC(1, 2, 2, 4, 64, 3) : W4_DEC(1, 1, 2, 4, 64, 3);
     }
 #undef W4_DEC
     return hipGetLastError();
