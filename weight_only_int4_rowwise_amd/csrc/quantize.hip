@@ -8,21 +8,25 @@
 //   q[c] = clamp(round_half_even(W[r][c] / s), -7, 7),  0 if s == 0
 //   packed two codes per byte (layout in include/w4a16.h).
 //
-// One 256-thread workgroup owns one row.  Each thread loads its 16-byte
-// chunks of the row once (coalesced), keeps them in registers, and the
-// absmax is reduced across the wavefront with cross-lane shuffles and across
-// the four wavefronts through LDS.  The codes are formed from the registers,
-// so HBM is read once and written once (2k + k/2 + 2 bytes per row).
+// Rows are spread over one, two or four wavefronts (by row length).  Each
+// lane loads its 16-byte chunks of the row once (coalesced, unconditional
+// range-checked loads, several rows in flight per compute unit) and keeps
+// them in registers; the absmax is reduced across the wavefront with
+// cross-lane shuffles and across the row's wavefronts through LDS.  The
+// codes are formed from the registers, so HBM is read once and written
+// once (2k + k/2 + 2 bytes per row).
 //
 // Exactness.  |w| as a bit pattern (sign cleared) orders like its value for
 // finite inputs, so the absmax is an integer max.  a / 7 is a correctly
 // rounded fp32 division, and fp32 -> fp16 rounding after it gives the
 // correctly rounded fp16 quotient (24 >= 2 * 11 + 2 bits, so the double
-// rounding is harmless).  For the codes, r = |w| * (1/s) is within 2^-20 of
-// the exact quotient |w| / s (for quotients <= 16); a quotient of two fp16
+// rounding is harmless).  For the codes, r = w * (1/s) is within 2^-20 of
+// the exact quotient Q = w / s (|Q| <= 10.5).  A quotient of two fp16
 // numbers that is not a half-integer lies at least 2^-12 from every
-// half-integer, so rounding r gives the exact result, and |r - (j + 1/2)| <
-// 2^-13 identifies an exact tie, which goes to the even neighbour.
+// half-integer, while an exact tie is a multiple of 2^-12.  So rounding r
+// to the nearest multiple of 2^-12 returns Q itself for a tie and stays on
+// Q's side of every half-integer otherwise, and rounding that to an
+// integer, ties to even, gives round_half_even(Q).
 #include "common.hpp"
 
 namespace w4a16 {
@@ -66,69 +70,95 @@ __device__ __forceinline__ RowScale make_scale(uint32_t amax_bits)
     return rs;
 }
 
-// Code of one fp16 weight (bit pattern) as a 4-bit two's-complement nibble.
-__device__ __forceinline__ uint32_t code_nibble(uint32_t wbits, const RowScale &rs)
+// Two's-complement nibble of the code of one weight (fp32 value wf), in 8
+// VALU ops: r = wf / s; snap r to the 2^-12 grid ((r + 3072) - 3072 rounds
+// to a multiple of 2^-12 for |r| < 1024); clamp to [-7, 7] (v_med3); adding
+// 2^23 + 16 rounds to an integer, ties to even, and leaves (q + 16) in the
+// low mantissa bits, whose low nibble is q mod 16.  s == 0 has inv == 0 and
+// gives code 0.
+__device__ __forceinline__ uint32_t code_nibble_f(float wf, float inv)
 {
-    const float mag = half_bits_to_float((uint16_t)(wbits & 0x7FFFu));
-    const float r = mag * rs.inv;
-    const float fl = floorf(r);
-    const float d = r - fl - 0.5f;
-    // exact tie -> even neighbour; otherwise nearest
-    float c = fabsf(d) < 0x1p-13f ? fl + (float)((int)fl & 1) : rintf(r);
-    c = fminf(c, 7.0f);
-    int q = (int)c;
-    if (rs.s == 0.0f)
-        q = 0;
-    if (wbits & 0x8000u)
-        q = -q;
-    return (uint32_t)q & 0xFu;
+    const float r = wf * inv;
+    const float snap = __fsub_rn(__fadd_rn(r, 3072.0f), 3072.0f);
+    const float c = __builtin_amdgcn_fmed3f(snap, -7.0f, 7.0f);
+    return __builtin_bit_cast(uint32_t, __fadd_rn(c, 8388624.0f)) & 0xFu;
 }
 
-// Register-resident path: the row fits in kQThreads * 8 * CHUNKS halves.
-// Requires k % 8 == 0 (16-byte chunks) and 16-byte aligned row starts.
-template <int CHUNKS>
+__device__ __forceinline__ uint32_t code_nibble(uint32_t wbits, const RowScale &rs)
+{
+    return code_nibble_f(half_bits_to_float((uint16_t)wbits), rs.inv);
+}
+
+// Eight codes of one 16-byte chunk (4 dwords of fp16 pairs) as one packed
+// dword: element 2j in the low nibble of byte j, 2j + 1 in its high nibble.
+__device__ __forceinline__ uint32_t pack_chunk(u32x4 v, float inv)
+{
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out |= code_nibble_f(half_bits_to_float((uint16_t)(v[j] & 0xFFFFu)), inv) << (8 * j);
+        out |= code_nibble_f(half_bits_to_float((uint16_t)(v[j] >> 16)), inv) << (8 * j + 4);
+    }
+    return out;
+}
+
+// Register-resident path: WPR wavefronts per row, CH 16-byte chunks per lane
+// (rows of up to 512 WPR CH halves).  Chunk c of wave part p of the row is
+// chunk (c WPR + p) 64 + lane, so every load and store instruction covers
+// consecutive memory.  Requires k % 8 == 0.
+template <int WPR, int CH>
 __global__ __launch_bounds__(kQThreads) void quantize_rows_reg(const uint16_t *__restrict__ w,
-                                                               int64_t k,
+                                                               int64_t n, int64_t k,
                                                                uint8_t *__restrict__ packed,
                                                                uint16_t *__restrict__ scales)
 {
-    __shared__ uint32_t lds4[4];
-    const int64_t row = blockIdx.x;
-    const uint16_t *wr = w + row * k;
-    uint8_t *pr = packed + row * (k / 2);
+    constexpr int RPW = (kQThreads / kWave) / WPR;          // rows per workgroup
+    __shared__ uint32_t lds4[kQThreads / kWave];
+    const int lane = threadIdx.x % kWave;
+    // uniform: keeps the row's buffer descriptor in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int part = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const bool live = row < n;                             // uniform per wave
+    const int64_t rowc = live ? row : n - 1;               // keeps the loads in range
     const int64_t nchunk = k / 8;
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(w + rowc * k, k * 2);
 
-    u32x4 v[CHUNKS];
+    u32x4 v[CH];
     uint32_t m = 0;
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const int64_t idx = (int64_t)c * kQThreads + threadIdx.x;
-        if (idx < nchunk) {
-            v[c] = load_stream16(reinterpret_cast<const uint8_t *>(wr + idx * 8));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                m = max(m, v[c][j] & 0x7FFFu);
-                m = max(m, (v[c][j] >> 16) & 0x7FFFu);
-            }
-        }
+    for (int c = 0; c < CH; ++c) {
+        const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+        v[c] = buf_load16_stream(rs_w, idx < nchunk ? (uint32_t)(idx * 16) : kOutOfRange);
     }
-    const uint32_t amax = block_max_u32(m, lds4);
-    const RowScale rs = make_scale(amax);
-    if (threadIdx.x == 0)
-        scales[row] = rs.bits;
-
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const int64_t idx = (int64_t)c * kQThreads + threadIdx.x;
-        if (idx < nchunk) {
-            uint32_t out = 0;
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                out |= code_nibble(v[c][j] & 0xFFFFu, rs) << (8 * j);
-                out |= code_nibble(v[c][j] >> 16, rs) << (8 * j + 4);
-            }
-            *reinterpret_cast<uint32_t *>(pr + idx * 4) = out;
+        for (int j = 0; j < 4; ++j) {
+            m = max(m, v[c][j] & 0x7FFFu);
+            m = max(m, (v[c][j] >> 16) & 0x7FFFu);
         }
+    m = wave_max_u32(m);
+    if (WPR > 1) {
+        if (lane == 0)
+            lds4[wave] = m;
+        __syncthreads();
+        const int w0 = wave - part;
+#pragma unroll
+        for (int p = 0; p < WPR; ++p)
+            m = max(m, lds4[w0 + p]);
+    }
+    const RowScale rs = make_scale(m);
+    if (live && part == 0 && lane == 0)
+        scales[row] = rs.bits;
+    if (!live)
+        return;
+    uint32_t *pr = reinterpret_cast<uint32_t *>(packed + row * (k / 2));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+        if (idx < nchunk)
+            pr[idx] = pack_chunk(v[c], rs.inv);
     }
 }
 
@@ -168,24 +198,36 @@ hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, vo
     const uint16_t *wp = static_cast<const uint16_t *>(w);
     uint8_t *pp = static_cast<uint8_t *>(packed);
     uint16_t *sp = static_cast<uint16_t *>(scales);
-    const dim3 grid((unsigned)n), block(kQThreads);
-    if (k % 8 == 0) {
-        const int64_t chunks = (k / 8 + kQThreads - 1) / kQThreads;
-        if (chunks <= 1)
-            hipLaunchKernelGGL(quantize_rows_reg<1>, grid, block, 0, stream, wp, k, pp, sp);
-        else if (chunks <= 2)
-            hipLaunchKernelGGL(quantize_rows_reg<2>, grid, block, 0, stream, wp, k, pp, sp);
-        else if (chunks <= 4)
-            hipLaunchKernelGGL(quantize_rows_reg<4>, grid, block, 0, stream, wp, k, pp, sp);
-        else if (chunks <= 8)
-            hipLaunchKernelGGL(quantize_rows_reg<8>, grid, block, 0, stream, wp, k, pp, sp);
-        else if (chunks <= 16)
-            hipLaunchKernelGGL(quantize_rows_reg<16>, grid, block, 0, stream, wp, k, pp, sp);
+    // lanes' chunks per row: at most 16 per lane, spread over 1, 2 or 4 waves
+    const int64_t lane_chunks = (k / 8 + kWave - 1) / kWave;
+#define W4_QREG(WPR, CH)                                                                           \
+    hipLaunchKernelGGL((quantize_rows_reg<WPR, CH>),                                               \
+                       dim3((unsigned)((n + (4 / WPR) - 1) / (4 / WPR))), dim3(kQThreads), 0,       \
+                       stream, wp, n, k, pp, sp)
+    if (k % 8 == 0 && lane_chunks <= 64) {
+        if (lane_chunks <= 1)
+            W4_QREG(1, 1);
+        else if (lane_chunks <= 2)
+            W4_QREG(1, 2);
+        else if (lane_chunks <= 4)
+            W4_QREG(1, 4);
+        else if (lane_chunks <= 8)
+            W4_QREG(1, 8);
+        else if (lane_chunks <= 16)
+            W4_QREG(1, 16);
+        else if (lane_chunks <= 24)
+            W4_QREG(2, 12);
+        else if (lane_chunks <= 32)
+            W4_QREG(2, 16);
+        else if (lane_chunks <= 48)
+            W4_QREG(4, 12);
         else
-            hipLaunchKernelGGL(quantize_rows_generic, grid, block, 0, stream, wp, k, pp, sp);
+            W4_QREG(4, 16);
     } else {
-        hipLaunchKernelGGL(quantize_rows_generic, grid, block, 0, stream, wp, k, pp, sp);
+        hipLaunchKernelGGL(quantize_rows_generic, dim3((unsigned)n), dim3(kQThreads), 0, stream,
+                           wp, k, pp, sp);
     }
+#undef W4_QREG
     return hipGetLastError();
 }
 
