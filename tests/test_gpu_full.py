@@ -158,3 +158,39 @@ def test_prefill_ffn_up_plain_sampled(prefill_data):
     y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "prefill FFN-up plain")
     print(f"prefill FFN-up plain: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
+# ----------------------------------------------------- largest accepted size
+
+def test_largest_accepted_weight():
+    """A weight whose packed form is just under the 2 GiB buffer limit the
+    kernels address (131040 x 32768: 2 146 959 360 bytes, also as prepacked
+    tiles).  Quantized bytes and scales compared in full; decode (m = 8),
+    fused GeGLU (m = 8, f = 65520) and prefill (m = 80) on sampled outputs
+    of every output tile, row-major and prepacked."""
+    n, k = 131040, 32768
+    assert w4.w4a16_prepacked_bytes(n, k) < 2 ** 31 and n * k // 2 < 2 ** 31
+    g = synth.generator(77, DEV)
+    w = synth.weight(n, k, g, device=DEV)
+    q, s, p_ref, s_ref = _quantize_checked(w, f"largest {n}x{k}")
+    del w
+    qp = w4.w4a16_prepack(q)
+    for m, tile_m in ((8, 16), (80, 128)):
+        x = synth.activations(m, k, g, DEV)
+        announce("largest linear", m, n, k)
+        mi, ni = _sample_indices(m, n, tile_m, 256, 10 + m)
+        y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+        for name, y in (("row-major", w4.w4a16_linear(x, q, s)),
+                        ("prepacked", w4.w4a16_linear_prepacked(x, qp, s))):
+            torch.cuda.synchronize()
+            r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag),
+                              f"largest m={m} {name}")
+            print(f"largest {n}x{k} m={m} {name}: {mi.size} sampled outputs, max err/bound {r:.4f}")
+            del y
+    x = synth.activations(8, k, g, DEV)
+    mi, ni = _sample_indices(8, n // 2, 16, 256, 30)
+    gr, a, b, ma, mb = oracle.geglu_at(bits(x), p_ref, s_ref, mi, ni)
+    y = w4.w4a16_geglu_linear_prepacked(x, qp, s)
+    torch.cuda.synchronize()
+    r = assert_within(_gather(y, mi, ni), gr, oracle.geglu_bound(gr, a, b, ma, mb), "largest GeGLU m=8")
+    print(f"largest GeGLU m=8: {mi.size} sampled outputs, max err/bound {r:.4f}")
