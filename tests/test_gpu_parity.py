@@ -280,6 +280,24 @@ def test_prefill_one_hot_and_pow2_bit_exact(m):
     _pow2_case(m, 260, 1024, 800 + m)
 
 
+@pytest.mark.parametrize("geglu", [False, True])
+def test_prefill_64_token_tiles(geglu):
+    """A grid that fills a tenth of one wave of workgroups with 128-token
+    tiles (13 output tiles x 4 token tiles) takes 64-token tiles; ragged
+    rows, tokens and k."""
+    g = synth.generator(1800 + geglu)
+    m, k = 500, 160
+    n = 3328 - 6 if not geglu else 2 * 1661
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill 64-token tiles n={n}")
+    if geglu:
+        check_geglu(x, q, s, p_ref, s_ref, f"prefill 64-token tiles geglu {m}x{n // 2}x{k}", bias)
+    else:
+        check_linear(x, q, s, p_ref, s_ref, f"prefill 64-token tiles {m}x{n}x{k}", bias)
+
+
 @pytest.mark.parametrize("m,f,k", [(65, 100, 256), (200, 300, 1024), (257, 64, 64)])
 def test_prefill_geglu_small(m, f, k):
     g = synth.generator(900 + m)

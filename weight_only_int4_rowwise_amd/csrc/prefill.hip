@@ -274,15 +274,52 @@ static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const vo
     return hipGetLastError();
 }
 
+// Fraction of the last wave of workgroups that is filled, two resident
+// workgroups per compute unit (64 KB of LDS each).
+static double wave_fill(int64_t grid, int64_t slots)
+{
+    const int64_t waves = (grid + slots - 1) / slots;
+    return (double)grid / (double)(waves * slots);
+}
+
+static int64_t compute_units()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
+
+template <bool GEGLU, bool TILED>
+static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, const void *packed,
+                                        const void *scales, int64_t n_out, const void *bias,
+                                        void *y, hipStream_t stream)
+{
+    // 128-token tiles (each dequantized operand feeds 8 MFMAs) unless the
+    // grid would leave the last wave of workgroups badly filled and the
+    // reduction is short: then 64-token tiles (measured: attention-out
+    // 12288 x 12288 at m = 2048, 1248 against 1054 TFLOP/s).
+    constexpr int out_per = 4 * 16 * (GEGLU ? 2 : 4);
+    const int64_t tiles_n = (n_out + out_per - 1) / out_per;
+    const int64_t slots = 2 * compute_units();
+    const double fill8 = wave_fill(tiles_n * ((m + 127) / 128), slots);
+    const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
+    if (k <= 16384 && fill4 > fill8 + 0.1)
+        return launch_prefill_t<4, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+}
+
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
                           bool tiled, hipStream_t stream)
 {
     if (geglu)
-        return tiled ? launch_prefill_t<4, 8, true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                     : launch_prefill_t<4, 8, true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
-    return tiled ? launch_prefill_t<4, 8, false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                 : launch_prefill_t<4, 8, false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return tiled ? launch_prefill_layout<true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                     : launch_prefill_layout<true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+    return tiled ? launch_prefill_layout<false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
+                 : launch_prefill_layout<false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
 }
 
 }  // namespace w4a16
