@@ -80,24 +80,31 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     static_assert(!GEGLU || NGW % 2 == 0, "GeGLU pairs gate and value row groups");
     constexpr int KS = 4 / RG;
     constexpr int KC = 128 * KU;              // reduction indices per chunk
-    constexpr int LD = KC + 8;                // LDS row stride (halves): +16 bytes against bank conflicts
     constexpr int RP = KC / 8;                // 16-byte pieces per activation row per chunk
-    constexpr int NPC = KS * MR * RP;         // activation pieces per round
-    constexpr int XP = (NPC + 4 * kWave - 1) / (4 * kWave);   // per thread
-    static_assert(NPC % (4 * kWave) == 0 || NPC < 4 * kWave, "activation pieces must divide evenly");
+    // Several token blocks: activations by LDS DMA into XOR-swizzled rows.
+    // One block: through registers into padded rows (measured faster there).
+    constexpr bool XDMA = MB > 1;
+    constexpr int LD = XDMA ? KC : KC + 8;    // row stride (halves)
+    constexpr int SLOT = MR * LD * 2;         // bytes of one chunk slot (MR rows)
+    constexpr int STAGE = KS * SLOT;          // bytes of one round's activations
+    constexpr int NCH = STAGE / 1024;         // 1 KB DMA loads per round
+    constexpr int NPC = KS * MR * RP;         // 16-byte activation pieces per round
+    constexpr int NXI = XDMA ? (NCH + 3) / 4 : (NPC + 4 * kWave - 1) / (4 * kWave);   // per wave / thread
+    static_assert(!XDMA || NCH * 1024 == STAGE, "activation round must split into 1 KB loads");
+    static_assert(XDMA || NPC % (4 * kWave) == 0 || NPC < 4 * kWave,
+                  "activation pieces must divide evenly");
     static_assert(D % 2 == 0, "the LDS double buffer alternates with the round parity");
     constexpr int CH = MB == 1 ? 2 : 1;       // independent accumulator chains per (group, block)
     constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;   // outputs per wave
     // LDS: the double-buffered activation chunks during the loop, the
     // partial sums of K-parts 1..KS-1 after it (one buffer, two uses)
     constexpr int kSlot = NGW * MB * kWave * 4;            // partial-sum floats per wave
-    constexpr int kXBytes = 2 * KS * MR * LD * 2;
+    constexpr int kXBytes = 2 * STAGE;
     constexpr int kRedBytes = (KS - 1) * RG * kSlot * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kXBytes > kRedBytes ? kXBytes : kRedBytes];
-    auto &xs = *reinterpret_cast<uint16_t(*)[2][KS][MR][LD]>(lds);
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kXBytes > kRedBytes ? kXBytes : kRedBytes];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int rgi = wave % RG;
     const int kp = wave / RG;
     const int r16 = lane % 16;
@@ -159,38 +166,85 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
             }
         }
     };
-    // activation pieces of a round: (chunk slot, row < MR, piece) over 256 threads
-    u32x4 xr[XP];
-    uint32_t xbase[XP], xcol[XP];
+    // Activation tile of a round: KS chunk slots (one per K-part) of MR
+    // token rows x KC indices, row-major; tokens past m repeat token m - 1.
+    //  * XDMA: rows of 256 KU bytes; the 16-byte piece P (indices 8 P ..
+    //    8 P + 7 of the chunk) of row r is stored at piece P ^ (r mod 16), so
+    //    the 16 rows an MFMA B-operand read touches start at different
+    //    banks.  DMA load i of this wave is the round's 1 KB load c = wave +
+    //    4 i; lane l fills 16-byte unit 64 c + l (whole row segments, so a
+    //    load covers few cache lines).
+    //  * otherwise: each thread loads pieces into registers at the top of a
+    //    round and stores them into rows padded by 16 bytes at its end.
+    uint32_t xbase[NXI], xcol[NXI];
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-        // threads past the last piece repeat one (same value, same LDS address)
-        const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
-        const int q = idx / RP;                       // slot * MR + row
-        const int mi = q % MR < m ? q % MR : m - 1;   // tokens past m repeat token m - 1
-        xcol[i] = (uint32_t)((q / MR) * KC + 8 * (idx % RP));   // index within the round
+    for (int i = 0; i < NXI; ++i) {
+        int slot, row, piece;
+        if (XDMA) {
+            const int u = 64 * (wave + 4 * i) + lane;      // 16-byte unit of the round
+            slot = u / (MR * RP);
+            row = (u % (MR * RP)) / RP;
+            piece = (u % RP) ^ (row & 15);
+        } else {
+            // threads past the last piece repeat one (same value, same LDS address)
+            const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
+            slot = idx / RP / MR;
+            row = (idx / RP) % MR;
+            piece = idx % RP;
+        }
+        const int mi = row < m ? row : m - 1;
+        xcol[i] = (uint32_t)(slot * KC + 8 * piece);       // index within the round
         xbase[i] = (uint32_t)(mi * k * 2 + 2 * xcol[i]);
     }
-    auto load_x = [&](int64_t r) {
+    u32x4 xr[XDMA ? 1 : NXI];
+    // Offsets below 2^31 plus kOutOfRange stay below 2^32 and out of range.
+    auto load_x = [&](int64_t r, int buf) {
         const uint32_t k0 = (uint32_t)(r * KS * KC);
         const uint32_t step = r < rounds ? 2 * k0 : kOutOfRange;
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
+        for (int i = 0; i < NXI; ++i) {
+            if (XDMA && NCH % 4 != 0 && wave + 4 * i >= NCH)
+                break;
             uint32_t off = xbase[i] + step;
             if (!EVEN && k0 + xcol[i] >= k32)
                 off = kOutOfRange;
-            xr[i] = buf_load16(xrs, off);
+            if constexpr (XDMA)
+                buf_load16_lds(xrs, off, lds + buf * STAGE + 1024 * (wave + 4 * i));
+            else
+                xr[i] = buf_load16(xrs, off);
         }
     };
     auto store_x = [&](int buf) {
+        if constexpr (!XDMA) {
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
-            const int q = idx / RP;
-            *reinterpret_cast<u32x4 *>(&xs[buf][q / MR][q % MR][8 * (idx % RP)]) = xr[i];
+            for (int i = 0; i < NXI; ++i) {
+                const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
+                *reinterpret_cast<u32x4 *>(lds + buf * STAGE + (idx / RP / MR) * SLOT +
+                                           ((idx / RP) % MR) * LD * 2 + 16 * (idx % RP)) = xr[i];
+            }
+        }
+    };
+    // XDMA: loads retire in order and each round issues its activation DMA
+    // before its weight loads, so waiting until at most NGW KU loads are
+    // outstanding means this wave's DMA of the next round has landed; the
+    // barrier then publishes it and retires the buffer the following DMA
+    // overwrites (the fences order only LDS accesses around it).
+    auto publish = [&]() {
+        if constexpr (XDMA) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        } else {
+            __syncthreads();
         }
     };
     const int brow = r16 < MR ? r16 : MR - 1;          // MFMA columns past MR repeat row MR - 1
+    const uint8_t *xrd = lds + kp * SLOT + brow * LD * 2;
+    uint32_t rdoff[4];                                 // piece 4 g + t of row brow
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        rdoff[t] = 16 * (XDMA ? ((4 * g + t) ^ brow) : 4 * g + t);
     auto compute = [&](int buf, const u32x4(&wd)[NGW][KU]) {
 #pragma unroll
         for (int p = 0; p < KU; ++p)
@@ -200,7 +254,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
 #pragma unroll
                 for (int b = 0; b < MB; ++b)
                     bx[b] = as_half8(*reinterpret_cast<const u32x4 *>(
-                        &xs[buf][kp][16 * b + brow][32 * g + 128 * p + 8 * t]));
+                        xrd + buf * STAGE + (16 * b * LD + 128 * p) * 2 + rdoff[t]));
 #pragma unroll
                 for (int j = 0; j < NGW; ++j) {
                     const half8 a = dequant8_of<TILED>(wd[j][p][t]);
@@ -218,25 +272,28 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     // top, activations first: left alone, the compiler sinks them towards
     // their first use and the prefetch distance collapses.
     u32x4 wr[D][NGW][KU];
-    load_x(0);
+    load_x(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D - 1; ++i)
         load_w(i, wr[i]);
+    if constexpr (XDMA)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU * (D - 1)));
     store_x(0);
-    __syncthreads();
+    publish();
     for (int64_t r0 = 0; r0 < rounds; r0 += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
             const int64_t r = r0 + i;
             if (r >= rounds)
                 break;
-            load_x(r + 1);
+            load_x(r + 1, (i & 1) ^ 1);
             __builtin_amdgcn_sched_barrier(0);
             load_w(r + D - 1, wr[(i + D - 1) % D]);
             __builtin_amdgcn_sched_barrier(0);
             compute(i & 1, wr[i]);
             store_x((i & 1) ^ 1);
-            __syncthreads();
+            publish();
         }
     }
     if (CH > 1) {
