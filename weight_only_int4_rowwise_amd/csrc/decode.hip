@@ -431,7 +431,7 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
             tall == 2 ? W4_DEC(2, 4, 2, 1, 16, 2)
                       : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(2, 1, 2, 1, 16, 3);
         else if (m <= 32)
-            tall == 2 ? W4_DEC(2, 4, 2, 2, 32, 2)
+            tall == 2 ? W4_DEC(1, 2, 2, 2, 32, 4)
                       : tall ? W4_DEC(1, 2, 2, 2, 32, 3) : W4_DEC(2, 1, 2, 2, 32, 3);
         else if (m <= 48)
             tall == 2 ? W4_DEC(1, 2, 2, 3, 48, 4)
