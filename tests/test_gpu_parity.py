@@ -213,6 +213,52 @@ def test_geglu_fused_matches_unfused_halves():
     assert torch.all((fused - unfused).abs() <= tol)
 
 
+# ------------------------------------------------ every decode launch class
+# The decode launch shape depends on the token class (m <= 1, 4, 8, 16, 32,
+# 48, 64) and on the weight height (under 24576 rows, under 49152, more).
+# One weight per height class, every token class, a reduction length that
+# is a whole number of rounds for every shape of that class (the
+# instantiations without per-index checks), and both weight layouts.
+
+_CLASS_MS = [1, 3, 8, 12, 17, 32, 45, 64]
+
+
+@pytest.mark.parametrize("n,k", [(1000, 2048), (36848, 1024), (65520, 1024)])
+def test_decode_every_launch_class(n, k):
+    g = synth.generator(1800 + n)
+    w = synth.weight(n, k, g, "t4")
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"class n={n} k={k}")
+    qp = w4.w4a16_prepack(q)
+    for m in _CLASS_MS:
+        x = synth.activations(m, k, g)
+        check_linear(x, q, s, p_ref, s_ref, f"class {m}x{n}x{k} bias", bias)
+        announce("class prepacked", m, n, k)
+        xd, bd = x.to(DEV), bias.to(DEV)
+        y0 = w4.w4a16_linear(xd, q, s, bd)
+        y1 = w4.w4a16_linear_prepacked(xd, qp, s, bd)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(y1), bits(y0), f"class prepacked vs row-major {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("f,k", [(496, 2048), (32752, 1024)])
+def test_decode_geglu_every_launch_class(f, k):
+    g = synth.generator(1900 + f)
+    w = synth.weight(2 * f, k, g, "t4")
+    bias = synth.normal_fp16((2 * f,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"geglu class f={f} k={k}")
+    qp = w4.w4a16_prepack(q)
+    for m in _CLASS_MS:
+        x = synth.activations(m, k, g)
+        check_geglu(x, q, s, p_ref, s_ref, f"geglu class {m}x{f}x{k} bias", bias)
+        announce("geglu class prepacked", m, f, k)
+        xd, bd = x.to(DEV), bias.to(DEV)
+        y0 = w4.w4a16_geglu_linear(xd, q, s, bd)
+        y1 = w4.w4a16_geglu_linear_prepacked(xd, qp, s, bd)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(y1), bits(y0), f"geglu class prepacked vs row-major {m}x{f}x{k}")
+
+
 # ---------------------------------------- tall weights at 32 < m <= 64
 # QKV-, FFN-up- and GeGLU-shaped weights (36864 / 65536 rows, 2 x 32768)
 # take their own decode launch shapes at 32 < m <= 64 (several row groups

@@ -35,9 +35,9 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 //
 // A wavefront owns NGW groups of 16 weight rows (for GeGLU: NGW / 2 gate
 // groups and the matching value groups) and MB blocks of 16 tokens.  A
-// workgroup of 4 wavefronts holds RG such row sets; the KS = 4 / RG
-// wavefronts of a row set split the reduction into interleaved chunks of
-// 128 KU indices.  A wavefront streams its rows chunk by chunk (KU 16-byte
+// workgroup of W wavefronts (4 to 16) holds RG such row sets; the KS =
+// W / RG wavefronts of a row set split the reduction into interleaved
+// chunks of 128 KU indices.  A wavefront streams its rows chunk by chunk (KU 16-byte
 // pieces per lane per row group), with a ring of D register sets so the
 // pieces of the next D - 1 chunks are in flight while the current one is
 // multiplied.  Each dequantized A operand feeds MB MFMAs (one per token
@@ -45,8 +45,8 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 //
 // The activation chunks of a round (KS chunks, MR x 128 KU fp16 each; MR =
 // m rounded up to 4, 8 or 16 for one block, 16 MB otherwise) are loaded
-// once per workgroup and double-buffered in LDS, one barrier per round; the RG wavefronts that
-// work on the same chunk share it.  Each round's activation loads are
+// once per workgroup and double-buffered in LDS, one barrier per round;
+// the RG wavefronts that work on the same chunk share it.  Each round's activation loads are
 // issued before its weight loads: vector loads retire in order, so waiting
 // for the activations does not wait for the weights.  Partial sums of the
 // KS wavefronts of a row set meet in LDS in a fixed order.
@@ -70,15 +70,16 @@ struct TokenTile {
     static_assert(MB == 1 ? (MR == 4 || MR == 8 || MR == 16) : MR == 16 * MB, "token rows");
 };
 
-template <int KU, int RG, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
-__global__ __launch_bounds__(4 * kWave) void decode_kernel(
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+__global__ __launch_bounds__(W * kWave) void decode_kernel(
     const uint16_t *__restrict__ x, int m, int64_t k, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, int64_t n_out, const uint16_t *__restrict__ bias,
     uint16_t *__restrict__ y)
 {
     (void)TokenTile<MB, MR>{};
     static_assert(!GEGLU || NGW % 2 == 0, "GeGLU pairs gate and value row groups");
-    constexpr int KS = 4 / RG;
+    static_assert(W % RG == 0, "row sets split the wavefronts evenly");
+    constexpr int KS = W / RG;
     constexpr int KC = 128 * KU;              // reduction indices per chunk
     constexpr int RP = KC / 8;                // 16-byte pieces per activation row per chunk
     // Several token blocks: activations by LDS DMA into XOR-swizzled rows.
@@ -89,11 +90,9 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     constexpr int STAGE = KS * SLOT;          // bytes of one round's activations
     constexpr int NCH = STAGE / 1024;         // 1 KB DMA loads per round
     constexpr int NPC = KS * MR * RP;         // 16-byte activation pieces per round
-    constexpr int NXI = XDMA ? (NCH + 3) / 4 : (NPC + 4 * kWave - 1) / (4 * kWave);   // per wave / thread
+    constexpr int NXI = XDMA ? (NCH + W - 1) / W
+                             : (NPC + W * kWave - 1) / (W * kWave);   // per wave / thread
     static_assert(!XDMA || NCH * 1024 == STAGE, "activation round must split into 1 KB loads");
-    static_assert(XDMA || NPC % (4 * kWave) == 0 || NPC < 4 * kWave,
-                  "activation pieces must divide evenly");
-    static_assert(D % 2 == 0, "the LDS double buffer alternates with the round parity");
     constexpr int CH = MB == 1 ? 2 : 1;       // independent accumulator chains per (group, block)
     constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;   // outputs per wave
     // LDS: the double-buffered activation chunks during the loop, the
@@ -124,7 +123,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     uint32_t wbase[NGW];
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
-        int64_t o = GEGLU ? o0 + 16 * (j % (NGW / 2)) + r16 : o0 + 16 * j + r16;
+        int64_t o = o0 + 16 * (GEGLU ? j % (NGW / 2 > 0 ? NGW / 2 : 1) : j) + r16;
         if (!TILED && o >= n_out)
             o = n_out - 1;
         const int64_t row = (GEGLU && j >= NGW / 2) ? n_out + o : o;
@@ -181,13 +180,14 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     for (int i = 0; i < NXI; ++i) {
         int slot, row, piece;
         if (XDMA) {
-            const int u = 64 * (wave + 4 * i) + lane;      // 16-byte unit of the round
+            const int u = 64 * (wave + W * i) + lane;      // 16-byte unit of the round
             slot = u / (MR * RP);
             row = (u % (MR * RP)) / RP;
             piece = (u % RP) ^ (row & 15);
         } else {
-            // threads past the last piece repeat one (same value, same LDS address)
-            const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
+            // pieces are dealt round-robin; surplus threads repeat one
+            // (same value, same LDS address)
+            const int idx = (threadIdx.x + W * kWave * i) % NPC;
             slot = idx / RP / MR;
             row = (idx / RP) % MR;
             piece = idx % RP;
@@ -203,13 +203,13 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
         const uint32_t step = r < rounds ? 2 * k0 : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < NXI; ++i) {
-            if (XDMA && NCH % 4 != 0 && wave + 4 * i >= NCH)
+            if (XDMA && NCH % W != 0 && wave + W * i >= NCH)
                 break;
             uint32_t off = xbase[i] + step;
             if (!EVEN && k0 + xcol[i] >= k32)
                 off = kOutOfRange;
             if constexpr (XDMA)
-                buf_load16_lds(xrs, off, lds + buf * STAGE + 1024 * (wave + 4 * i));
+                buf_load16_lds(xrs, off, lds + buf * STAGE + 1024 * (wave + W * i));
             else
                 xr[i] = buf_load16(xrs, off);
         }
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
         if constexpr (!XDMA) {
 #pragma unroll
             for (int i = 0; i < NXI; ++i) {
-                const int idx = (threadIdx.x + 4 * kWave * i) % NPC;
+                const int idx = (threadIdx.x + W * kWave * i) % NPC;
                 *reinterpret_cast<u32x4 *>(lds + buf * STAGE + (idx / RP / MR) * SLOT +
                                            ((idx / RP) % MR) * LD * 2 + 16 * (idx % RP)) = xr[i];
             }
@@ -266,9 +266,9 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     };
 
     // Ring of D weight register sets: round r uses set r % D, loaded D - 1
-    // rounds earlier.  The round loop is unrolled D times so every set has
-    // a fixed register name (no copies, which would force the loads to
-    // retire early).  Scheduling barriers keep each round's loads at its
+    // rounds earlier.  The round loop is unrolled U times (a multiple of D
+    // and of the 2 LDS buffers) so every set has a fixed register name (no
+    // copies, which would force the loads to retire early).  Scheduling barriers keep each round's loads at its
     // top, activations first: left alone, the compiler sinks them towards
     // their first use and the prefetch distance collapses.
     u32x4 wr[D][NGW][KU];
@@ -281,9 +281,10 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU * (D - 1)));
     store_x(0);
     publish();
-    for (int64_t r0 = 0; r0 < rounds; r0 += D) {
+    constexpr int U = D % 2 == 0 ? D : 2 * D;
+    for (int64_t r0 = 0; r0 < rounds; r0 += U) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
+        for (int i = 0; i < U; ++i) {
             const int64_t r = r0 + i;
             if (r >= rounds)
                 break;
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
             __builtin_amdgcn_sched_barrier(0);
             load_w(r + D - 1, wr[(i + D - 1) % D]);
             __builtin_amdgcn_sched_barrier(0);
-            compute(i & 1, wr[i]);
+            compute(i & 1, wr[i % D]);
             store_x((i & 1) ^ 1);
             publish();
         }
@@ -366,37 +367,42 @@ __global__ __launch_bounds__(4 * kWave) void decode_kernel(
     }
 }
 
-template <int KU, int RG, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
 void launch_decode_t(const void *x, int m, int64_t k, const void *packed, const void *scales,
                      int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
     constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;
     const unsigned grid = (unsigned)ceil_div(n_out, OUTW * RG);
-    hipLaunchKernelGGL((decode_kernel<KU, RG, D, MB, MR, NGW, EVEN, GEGLU, TILED>), dim3(grid),
-                       dim3(4 * kWave), 0, stream, static_cast<const uint16_t *>(x), m, k,
+    hipLaunchKernelGGL((decode_kernel<KU, RG, W, D, MB, MR, NGW, EVEN, GEGLU, TILED>),
+                       dim3(grid), dim3(W * kWave), 0, stream, static_cast<const uint16_t *>(x), m, k,
                        static_cast<const uint8_t *>(packed), static_cast<const uint16_t *>(scales),
                        n_out, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
 }
 
 // Reduction evenness of a launch.
-template <int KU, int RG, int D, int MB, int MR, int NGW, bool GEGLU, bool TILED>
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool GEGLU, bool TILED>
 void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const void *scales,
                      int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
-    if (k % (128 * KU * (4 / RG)) == 0)
-        launch_decode_t<KU, RG, D, MB, MR, NGW, true, GEGLU, TILED>(x, m, k, packed, scales, n_out,
-                                                                    bias, y, stream);
+    if (k % (128 * KU * (W / RG)) == 0)
+        launch_decode_t<KU, RG, W, D, MB, MR, NGW, true, GEGLU, TILED>(x, m, k, packed, scales,
+                                                                       n_out, bias, y, stream);
     else
-        launch_decode_t<KU, RG, D, MB, MR, NGW, false, GEGLU, TILED>(x, m, k, packed, scales,
-                                                                     n_out, bias, y, stream);
+        launch_decode_t<KU, RG, W, D, MB, MR, NGW, false, GEGLU, TILED>(x, m, k, packed, scales,
+                                                                        n_out, bias, y, stream);
 }
 
 // Launch shapes per token class and weight height (rows = n, or 2 f for
-// GeGLU), from sweeps over KU, RG, D and NGW on MI355X at the GLM-130B
-// shapes (12288, 36864 and 65536 rows; 12288 and 32768 columns): tall
-// matrices want more row groups per workgroup, short ones more reduction
-// splits (more wavefronts per row), and more token blocks want more row
-// groups per wavefront (each activation operand feeds more MFMAs).
+// GeGLU), from sweeps over KU, RG, W, D and NGW on MI355X at the GLM-130B
+// shapes (12288, 36864 and 65536 rows; 12288 and 32768 columns).  Each
+// workgroup reads the activations once for all its rows, so tall matrices
+// want many rows per workgroup, spread over more wavefronts (W up to 16)
+// rather than more row groups per wavefront (which costs registers and
+// occupancy); for the 36864-row QKV projection, 144 rows per workgroup
+// (3 row sets x 4 K-parts, 12 wavefronts) make exactly one workgroup per
+// CU.  Short matrices want more reduction splits (more wavefronts per
+// row), and more token blocks want more row groups per wavefront (each
+// activation operand feeds more MFMAs).
 template <bool GEGLU, bool TILED>
 static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const void *packed,
                                        const void *scales, int64_t n_out, const void *bias, void *y,
@@ -404,41 +410,44 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
 {
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
     const int tall = rows >= 49152 ? 2 : rows >= 24576 ? 1 : 0;
-#define W4_DEC(KU, RG, D, MB, MR, NGW)                                                            \
-    launch_decode_e<KU, RG, D, MB, MR, NGW, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, \
-                                                          stream)
+#define W4_DEC(KU, RG, W, D, MB, MR, NGW)                                                         \
+    launch_decode_e<KU, RG, W, D, MB, MR, NGW, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, \
+                                                             y, stream)
     if constexpr (GEGLU) {
         // a wavefront always holds gate and value groups: NGW even
         if (m <= 4)
-            tall == 2 ? W4_DEC(4, 4, 2, 1, 4, 2) : W4_DEC(2, 2, 2, 1, 4, 2);
+            tall == 2 ? W4_DEC(2, 4, 8, 2, 1, 4, 2) : W4_DEC(2, 2, 4, 2, 1, 4, 2);
         else if (m <= 8)
-            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 2) : W4_DEC(4, 2, 2, 1, 8, 2);
+            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 8, 2) : W4_DEC(4, 2, 4, 2, 1, 8, 2);
         else if (m <= 16)
-            tall == 2 ? W4_DEC(4, 4, 2, 1, 16, 2) : W4_DEC(4, 2, 2, 1, 16, 2);
+            tall == 2 ? W4_DEC(2, 8, 16, 2, 1, 16, 2) : W4_DEC(4, 2, 4, 2, 1, 16, 2);
         else if (m <= 32)
-            W4_DEC(2, 2, 2, 2, 32, 4);
+            tall == 2 ? W4_DEC(1, 4, 16, 2, 2, 32, 4) : W4_DEC(2, 2, 4, 2, 2, 32, 4);
         else if (m <= 48)
-            W4_DEC(1, 2, 2, 3, 48, 4);
+            tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4) : W4_DEC(1, 2, 4, 2, 3, 48, 4);
         else
-            tall == 2 ? W4_DEC(1, 2, 2, 4, 64, 4) : W4_DEC(2, 2, 2, 4, 64, 2);
+            tall == 2 ? W4_DEC(1, 8, 16, 2, 4, 64, 2) : W4_DEC(2, 2, 4, 2, 4, 64, 2);
     } else {
-        if (m <= 4)
-            tall == 2 ? W4_DEC(2, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 2, 1, 4, 1);
+        if (m <= 2)
+            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 4, 2, 1, 4, 1);
+        else if (m <= 4)
+            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1)
+                      : tall ? W4_DEC(2, 3, 6, 2, 1, 4, 1) : W4_DEC(2, 1, 4, 2, 1, 4, 1);
         else if (m <= 8)
-            tall == 2 ? W4_DEC(2, 4, 2, 1, 8, 1)
-                      : tall ? W4_DEC(1, 1, 2, 1, 8, 3) : W4_DEC(2, 1, 2, 1, 8, 3);
+            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 8, 1)
+                      : tall ? W4_DEC(1, 1, 4, 2, 1, 8, 3) : W4_DEC(4, 3, 12, 2, 1, 8, 1);
         else if (m <= 16)
-            tall == 2 ? W4_DEC(2, 4, 2, 1, 16, 2)
-                      : tall ? W4_DEC(2, 4, 2, 1, 16, 1) : W4_DEC(2, 1, 2, 1, 16, 3);
+            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
+                      : tall ? W4_DEC(2, 3, 12, 2, 1, 16, 3) : W4_DEC(2, 1, 8, 2, 1, 16, 3);
         else if (m <= 32)
-            tall == 2 ? W4_DEC(1, 2, 2, 2, 32, 4)
-                      : tall ? W4_DEC(1, 2, 2, 2, 32, 3) : W4_DEC(2, 1, 2, 2, 32, 3);
+            tall == 2 ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
+                      : tall ? W4_DEC(2, 3, 12, 2, 2, 32, 3) : W4_DEC(2, 1, 4, 2, 2, 32, 3);
         else if (m <= 48)
-            tall == 2 ? W4_DEC(1, 2, 2, 3, 48, 4)
-                      : tall ? W4_DEC(1, 2, 2, 3, 48, 3) : W4_DEC(1, 1, 2, 3, 48, 3);
+            tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
+                      : tall ? W4_DEC(1, 3, 12, 2, 3, 48, 3) : W4_DEC(1, 1, 4, 2, 3, 48, 3);
         else
-            tall == 2 ? W4_DEC(1, 2, 2, 4, 64, 4)
-                      : tall ? W4_DEC(1, 2, 2, 4, 64, 3) : W4_DEC(1, 1, 2, 4, 64, 3);
+            tall == 2 ? W4_DEC(1, 8, 16, 2, 4, 64, 2)
+                      : tall ? W4_DEC(1, 3, 12, 2, 4, 64, 3) : W4_DEC(1, 1, 4, 2, 4, 64, 3);
     }
 #undef W4_DEC
     return hipGetLastError();
