@@ -63,20 +63,24 @@ def csrc_hash():
     return h.hexdigest()[:16]
 
 
-def time_launches(torch, fn, reps, warm=2):
-    """Average duration (s) of fn() over reps back-to-back launches, timed
-    with events on the current stream (the stream the kernels run on)."""
+def time_launches(torch, fn, reps, warm=2, repeats=5):
+    """Duration (s) of one fn() call: the median over `repeats` timings of
+    reps back-to-back launches each, timed with events on the current stream
+    (the stream the kernels run on)."""
     for _ in range(warm):
         fn()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / 1e3 / reps
+    times = []
+    for _ in range(repeats):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e) / 1e3 / reps)
+    return sorted(times)[len(times) // 2]
 
 
 def make_rotating(torch, w4, synth, n, k, dist, count, seed0, dev):
