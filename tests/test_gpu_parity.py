@@ -370,6 +370,26 @@ def test_deterministic_reruns():
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), m
 
 
+def test_calls_follow_the_current_stream():
+    """The binding passes torch's current stream; results on a side stream
+    (default priority) equal those on the default stream."""
+    g = synth.generator(1100)
+    w = synth.weight(700, 2048, g).to(DEV)
+    xs = {m: synth.activations(m, 2048, g).to(DEV) for m in (8, 130)}
+    q, s = w4.quantize_rowwise_int4(w)
+    ref = {m: w4.w4a16_linear(x, q, s) for m, x in xs.items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q2, s2 = w4.quantize_rowwise_int4(w)
+        out = {m: w4.w4a16_linear(x, q2, s2) for m, x in xs.items()}
+    side.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+    for m in xs:
+        assert torch.equal(out[m].view(torch.int16), ref[m].view(torch.int16)), m
+
+
 def test_empty_and_rejected_calls():
     x = torch.zeros(0, 64, dtype=torch.float16, device=DEV)
     q = torch.zeros(16, 32, dtype=torch.uint8, device=DEV)

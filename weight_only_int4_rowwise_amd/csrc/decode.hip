@@ -4,9 +4,9 @@
 // card, "Method": linear_forward with the weights turned back into FP16 at
 // run time; paperlayer.ai summary, "INT4 Quantization for RTX 3090s/2080s").
 // At decode sizes the packed weights dominate the traffic (k/2 bytes per
-// row against 2 m k bytes of activations), so both kernels here are built
-// to stream the weights from HBM once at full bandwidth (one kernel
-// template below, shaped per token count):
+// row against 2 m k bytes of activations), so the kernel is built to stream
+// the weights from HBM once at full bandwidth (one template, shaped per
+// token count and weight height):
 //
 //  * Codes become exact fp16 integers in registers (dequant8: 9 VALU ops
 //    per 8 codes of the prepacked layout, 12 for the row-major one) and
@@ -14,9 +14,9 @@
 //    A operand and up to 16 tokens per MFMA as the B operand, fp32
 //    accumulation.  Padding m up to 16 costs idle MFMA slots, not bytes.
 //  * Every load is an unconditional range-checked buffer load (padding
-//    lanes read zeros), and the main loops are unrolled twice over two
-//    register sets, so the next stage's loads stay in flight while the
-//    current stage is multiplied (no register copies that would force the
+//    lanes read zeros), and the main loop is unrolled over a ring of
+//    register sets, so the next rounds' loads stay in flight while the
+//    current round is multiplied (no register copies that would force the
 //    loads to retire).
 //  * The row scale is constant along the sum, so it is applied once to the
 //    fp32 sum in the epilogue instead of to every weight; then the bias,
