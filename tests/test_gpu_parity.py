@@ -241,6 +241,41 @@ def test_decode_every_launch_class(n, k):
         assert_bits_equal(bits(y1), bits(y0), f"class prepacked vs row-major {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("n", [1001, 1002, 1003])
+def test_decode_rows_not_a_multiple_of_four(n):
+    """Output rows of n values lose 8-byte alignment when n % 4 != 0: every
+    launch class then stores and reads its scales and biases element-wise."""
+    g = synth.generator(2000 + n)
+    k = 1056
+    w = synth.weight(n, k, g, "t4")
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"n%4 n={n}")
+    qp = w4.w4a16_prepack(q)
+    for m in _CLASS_MS:
+        x = synth.activations(m, k, g)
+        check_linear(x, q, s, p_ref, s_ref, f"n%4 {m}x{n}x{k} bias", bias)
+        announce("n%4 prepacked", m, n, k)
+        xd, bd = x.to(DEV), bias.to(DEV)
+        y0 = w4.w4a16_linear(xd, q, s, bd)
+        y1 = w4.w4a16_linear_prepacked(xd, qp, s, bd)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(y1), bits(y0), f"n%4 prepacked vs row-major {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("f", [499, 502])
+def test_decode_geglu_halves_not_a_multiple_of_four(f):
+    """The value half of the scales and biases starts at entry f: with
+    f % 4 != 0 it is not 8-byte aligned."""
+    g = synth.generator(2100 + f)
+    k = 1056
+    w = synth.weight(2 * f, k, g, "t4")
+    bias = synth.normal_fp16((2 * f,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"geglu f%4 f={f}")
+    for m in _CLASS_MS:
+        x = synth.activations(m, k, g)
+        check_geglu(x, q, s, p_ref, s_ref, f"geglu f%4 {m}x{f}x{k} bias", bias)
+
+
 @pytest.mark.parametrize("f,k", [(496, 2048), (32752, 1024)])
 def test_decode_geglu_every_launch_class(f, k):
     g = synth.generator(1900 + f)

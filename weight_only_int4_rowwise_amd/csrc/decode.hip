@@ -65,6 +65,31 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 // wavefront reads KU KB of consecutive memory per chunk and row group
 // instead of 16 row segments of 64 KU bytes.
 // ---------------------------------------------------------------------------
+// Four consecutive fp16 values p[o .. o + 3] (o a multiple of 4), packed
+// two per word (0 for no p); entries at or past `count` repeat entry
+// count - 1 (their outputs are never stored).  `whole` says that p is 8-byte
+// aligned, a fact about the whole call: then one 8-byte load serves when all
+// four are in range.
+__device__ __forceinline__ uint2 load4_h(const uint16_t *__restrict__ p, int o, int count, bool whole)
+{
+    if (!p)
+        return uint2{0u, 0u};
+    if (whole && o + 3 < count)
+        return *reinterpret_cast<const uint2 *>(p + o);
+    uint32_t h[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        h[c] = p[o + c < count ? o + c : count - 1];
+    return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// Entry i (0..3) of four packed fp16 values, as a float.
+__device__ __forceinline__ float half4_at(uint2 v, int i)
+{
+    const uint32_t w = i < 2 ? v.x : v.y;
+    return half_bits_to_float((uint16_t)((i & 1) ? w >> 16 : w & 0xFFFFu));
+}
+
 template <int MB, int MR>
 struct TokenTile {
     static_assert(MB == 1 ? (MR == 4 || MR == 8 || MR == 16) : MR == 16 * MB, "token rows");
@@ -305,6 +330,36 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
                 acc[j][b][0] += acc[j][b][CH - 1];
     }
 
+    // The epilogue's row scales and biases: lane outputs o0 + 16 j + 4 g + i
+    // (i = 0..3, consecutive), loaded once, four at a time, by the waves that
+    // store.  With more than four token rows they are loaded before the
+    // K-part reduction, so their latency overlaps it; with four (m <= 4,
+    // where one lane in 16 or fewer stores) only the storing lanes load them,
+    // after it.
+    constexpr int NO = GEGLU ? NGW / 2 : NGW;   // output groups
+    constexpr int NV = GEGLU ? NO : 1;          // value groups (GeGLU)
+    constexpr bool EARLY = MR > 4;
+    // Callers pass scales, bias and y 16-byte aligned; rows of n_out fp16
+    // values keep 8-byte alignment when n_out is a multiple of 4.  Output
+    // indices stay below 2^31 (n_out <= 2^30).
+    const int n32 = (int)n_out;
+    const bool vec = n_out % 4 == 0;
+    uint2 sa[NO], ba[NO], sv[NV], bv[NV];
+    auto load_epilogue = [&]() {
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int ob = (int)o0 + 16 * j + 4 * g;
+            sa[j] = load4_h(scales, ob, n32, true);
+            ba[j] = load4_h(bias, ob, n32, true);
+            if constexpr (GEGLU) {
+                sv[j] = load4_h(scales + n_out, ob, n32, vec);
+                bv[j] = load4_h(bias ? bias + n_out : nullptr, ob, n32, vec);
+            }
+        }
+    };
+    if (EARLY && kp == 0)
+        load_epilogue();
+
     if (KS > 1) {
         // partial sums of K-parts 1..KS-1 -> LDS; K-part 0 adds them in order
         float *red = reinterpret_cast<float *>(lds);
@@ -333,37 +388,49 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
                             red[((q - 1) * RG + rgi) * kSlot + ((j * MB + b) * kWave + lane) * 4 + i];
     }
 
-    // lane holds D[4 g + i][r16] of (row group j, token block b):
-    // output row 4 g + i of the group, token 16 b + r16
+    // lane holds D[4 g + i][r16] of (row group j, token block b): outputs
+    // o0 + 16 j + 4 g + i of the wave for token 16 b + r16, i.e. four
+    // consecutive outputs, stored as one 8-byte write when all are in range
+    // and aligned
+    if (!EARLY) {
+        if (r16 >= m)
+            return;
+        load_epilogue();
+    }
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
         const int mi = 16 * b + r16;
         if (mi >= m)
             continue;
-        constexpr int NO = GEGLU ? NGW / 2 : NGW;   // output groups
 #pragma unroll
-        for (int j = 0; j < NO; ++j)
+        for (int j = 0; j < NO; ++j) {
+            const int ob = (int)o0 + 16 * j + 4 * g;
+            if (ob >= n32)
+                continue;
+            uint16_t h[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t o = o0 + 16 * j + 4 * g + i;
-                if (o >= n_out)
-                    continue;
                 float v;
-                if (GEGLU) {
-                    float a = acc[j][b][0][i] * half_bits_to_float(scales[o]);
-                    float bv = acc[j + NO][b][0][i] * half_bits_to_float(scales[n_out + o]);
-                    if (bias) {
-                        a += half_bits_to_float(bias[o]);
-                        bv += half_bits_to_float(bias[n_out + o]);
-                    }
-                    v = gelu_erf(a) * bv;
+                if constexpr (GEGLU) {
+                    const float a = acc[j][b][0][i] * half4_at(sa[j], i) + half4_at(ba[j], i);
+                    const float bb = acc[j + NO][b][0][i] * half4_at(sv[j], i) + half4_at(bv[j], i);
+                    v = gelu_erf(a) * bb;
                 } else {
-                    v = acc[j][b][0][i] * half_bits_to_float(scales[o]);
-                    if (bias)
-                        v += half_bits_to_float(bias[o]);
+                    v = acc[j][b][0][i] * half4_at(sa[j], i) + half4_at(ba[j], i);
                 }
-                y[(int64_t)mi * n_out + o] = float_to_half_bits(v);
+                h[i] = float_to_half_bits(v);
             }
+            uint16_t *dst = y + (int64_t)mi * n_out + ob;
+            if (vec && ob + 3 < n32) {
+                *reinterpret_cast<uint2 *>(dst) =
+                    uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (ob + i < n32)
+                        dst[i] = h[i];
+            }
+        }
     }
 }
 
@@ -428,9 +495,7 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
         else
             tall == 2 ? W4_DEC(1, 8, 16, 2, 4, 64, 2) : W4_DEC(2, 2, 4, 2, 4, 64, 2);
     } else {
-        if (m <= 2)
-            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1) : W4_DEC(2, 1, 4, 2, 1, 4, 1);
-        else if (m <= 4)
+        if (m <= 4)
             tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1)
                       : tall ? W4_DEC(2, 3, 6, 2, 1, 4, 1) : W4_DEC(2, 1, 4, 2, 1, 4, 1);
         else if (m <= 8)
