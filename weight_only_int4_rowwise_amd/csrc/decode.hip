@@ -386,6 +386,18 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
                     for (int i = 0; i < 4; ++i)
                         acc[j][b][0][i] +=
                             red[((q - 1) * RG + rgi) * kSlot + ((j * MB + b) * kWave + lane) * 4 + i];
+        // With 3 or more waves per SIMD (at most 168 registers) and 12 or
+        // more accumulator tiles per wave, pin the sums here: left alone, the
+        // compiler sinks each add into the epilogue's per-output branches,
+        // keeps every partial read live until then and spills 44 registers.
+        // Smaller shapes do not spill and measure faster without the pin.
+        if constexpr (W >= 12 && NGW * MB >= 12) {
+#pragma unroll
+            for (int j = 0; j < NGW; ++j)
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    asm volatile("" : "+v"(acc[j][b][0]));
+        }
     }
 
     // lane holds D[4 g + i][r16] of (row group j, token block b): outputs
