@@ -224,6 +224,18 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float v)
     return __builtin_bit_cast(uint16_t, (_Float16)v);   // round to nearest even
 }
 
+// An output's fp32 value to fp16 bits (round to nearest even) as a step of
+// its own.  The empty asm keeps the compiler from folding the multiply-add
+// that produced v into a mixed-precision instruction that rounds straight to
+// fp16: it does so in some kernel shapes and not in others, which would make
+// the rounding, and so the bits, depend on the launch shape and the weight
+// layout.  Every epilogue rounds the fp32 result, then to fp16.
+__device__ __forceinline__ uint16_t output_half_bits(float v)
+{
+    asm volatile("" : "+v"(v));
+    return float_to_half_bits(v);
+}
+
 // GELU in its defining form t * Phi(t) = t/2 * (1 + erf(t / sqrt 2)), with
 // the device math library's erff.
 __device__ __forceinline__ float gelu_erf(float t)

@@ -424,13 +424,13 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
             for (int i = 0; i < 4; ++i) {
                 float v;
                 if constexpr (GEGLU) {
-                    const float a = acc[j][b][0][i] * half4_at(sa[j], i) + half4_at(ba[j], i);
-                    const float bb = acc[j + NO][b][0][i] * half4_at(sv[j], i) + half4_at(bv[j], i);
+                    const float a = __builtin_fmaf(acc[j][b][0][i], half4_at(sa[j], i), half4_at(ba[j], i));
+                    const float bb = __builtin_fmaf(acc[j + NO][b][0][i], half4_at(sv[j], i), half4_at(bv[j], i));
                     v = gelu_erf(a) * bb;
                 } else {
-                    v = acc[j][b][0][i] * half4_at(sa[j], i) + half4_at(ba[j], i);
+                    v = __builtin_fmaf(acc[j][b][0][i], half4_at(sa[j], i), half4_at(ba[j], i));
                 }
-                h[i] = float_to_half_bits(v);
+                h[i] = output_half_bits(v);
             }
             uint16_t *dst = y + (int64_t)mi * n_out + ob;
             if (vec && ob + 3 < n32) {

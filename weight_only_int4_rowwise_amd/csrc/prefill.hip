@@ -215,21 +215,20 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t o = ob + i < n_out ? ob + i : n_out - 1;
+                // s acc + bias with one fp32 rounding (bias 0 when absent),
+                // as in the decode kernel
                 float v;
                 if (GEGLU) {
-                    float a = acc[j][b][i] * half_bits_to_float(scales[o]);
-                    float bv = acc[j + NO][b][i] * half_bits_to_float(scales[n_out + o]);
-                    if (bias) {
-                        a += half_bits_to_float(bias[o]);
-                        bv += half_bits_to_float(bias[n_out + o]);
-                    }
+                    const float a = __builtin_fmaf(acc[j][b][i], half_bits_to_float(scales[o]),
+                                                   bias ? half_bits_to_float(bias[o]) : 0.0f);
+                    const float bv = __builtin_fmaf(acc[j + NO][b][i], half_bits_to_float(scales[n_out + o]),
+                                                    bias ? half_bits_to_float(bias[n_out + o]) : 0.0f);
                     v = gelu_erf(a) * bv;
                 } else {
-                    v = acc[j][b][i] * half_bits_to_float(scales[o]);
-                    if (bias)
-                        v += half_bits_to_float(bias[o]);
+                    v = __builtin_fmaf(acc[j][b][i], half_bits_to_float(scales[o]),
+                                       bias ? half_bits_to_float(bias[o]) : 0.0f);
                 }
-                h[i] = float_to_half_bits(v);
+                h[i] = output_half_bits(v);
             }
             uint16_t *dst = y + mi * n_out + ob;
             if (vec && ob + 3 < n_out) {
