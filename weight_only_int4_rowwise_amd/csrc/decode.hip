@@ -481,7 +481,9 @@ void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const 
 // (3 row sets x 4 K-parts, 12 wavefronts) make exactly one workgroup per
 // CU.  Short matrices want more reduction splits (more wavefronts per
 // row), and more token blocks want more row groups per wavefront (each
-// activation operand feeds more MFMAs).
+// activation operand feeds more MFMAs).  At m > 48 tall weights keep three
+// weight register sets in flight (D = 3): the round there is long enough
+// that two sets leave the wave waiting on the loads.
 template <bool GEGLU, bool TILED>
 static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const void *packed,
                                        const void *scales, int64_t n_out, const void *bias, void *y,
@@ -505,7 +507,7 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
         else if (m <= 48)
             tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4) : W4_DEC(1, 2, 4, 2, 3, 48, 4);
         else
-            tall == 2 ? W4_DEC(1, 8, 16, 2, 4, 64, 2) : W4_DEC(2, 2, 4, 2, 4, 64, 2);
+            tall == 2 ? W4_DEC(1, 8, 16, 3, 4, 64, 2) : W4_DEC(2, 2, 4, 2, 4, 64, 2);
     } else {
         if (m <= 4)
             tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1)
@@ -523,8 +525,8 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
             tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
                       : tall ? W4_DEC(1, 3, 12, 2, 3, 48, 3) : W4_DEC(1, 1, 4, 2, 3, 48, 3);
         else
-            tall == 2 ? W4_DEC(1, 8, 16, 2, 4, 64, 2)
-                      : tall ? W4_DEC(1, 3, 12, 2, 4, 64, 3) : W4_DEC(1, 1, 4, 2, 4, 64, 3);
+            tall == 2 ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
+                      : tall ? W4_DEC(1, 3, 12, 3, 4, 64, 3) : W4_DEC(1, 1, 4, 2, 4, 64, 3);
     }
 #undef W4_DEC
     return hipGetLastError();
