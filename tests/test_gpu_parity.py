@@ -363,9 +363,9 @@ def test_prefill_one_hot_and_pow2_bit_exact(m):
 
 @pytest.mark.parametrize("geglu", [False, True])
 def test_prefill_64_token_tiles(geglu):
-    """A grid that fills a tenth of one wave of workgroups with 128-token
-    tiles (13 output tiles x 4 token tiles) takes 64-token tiles; ragged
-    rows, tokens and k."""
+    """A small grid (13 output tiles x 4 token tiles of the largest shape)
+    takes 64-token tiles (192 rows; GeGLU 64 outputs); ragged rows, tokens
+    and k."""
     g = synth.generator(1800 + geglu)
     m, k = 500, 160
     n = 3328 - 6 if not geglu else 2 * 1661
@@ -377,6 +377,34 @@ def test_prefill_64_token_tiles(geglu):
         check_geglu(x, q, s, p_ref, s_ref, f"prefill 64-token tiles geglu {m}x{n // 2}x{k}", bias)
     else:
         check_linear(x, q, s, p_ref, s_ref, f"prefill 64-token tiles {m}x{n}x{k}", bias)
+
+
+@pytest.mark.parametrize("geglu,m,n,k", [(False, 2000, 12280, 160), (False, 2000, 16380, 256),
+                                         (True, 2000, 2 * 4080, 160)])
+def test_prefill_large_grids(geglu, m, n, k):
+    """Grids of more than two 256-row x 128-token tiles per CU (on a
+    256-CU MI355X) take the 256-row tiles: 12280 rows at m = 2000 with
+    64-token tiles (768 large tiles fill 1.5 waves), 16380 rows with
+    128-token tiles (1024 fill 2 waves), and GeGLU with 128-token tiles
+    (f = 4080: ragged against 128-output tiles, a multiple of 16 as the
+    prepacked GeGLU layout requires).  Ragged tokens and k; both layouts."""
+    g = synth.generator(2200 + n + k)
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill large grid {m}x{n}x{k}")
+    if geglu:
+        check_geglu(x, q, s, p_ref, s_ref, f"prefill large grid geglu {m}x{n // 2}x{k}", bias)
+    else:
+        check_linear(x, q, s, p_ref, s_ref, f"prefill large grid {m}x{n}x{k}", bias)
+    announce("prefill large grid prepacked", m, n, k)
+    xd, bd = x.to(DEV), bias.to(DEV)
+    f0, f1 = ((w4.w4a16_geglu_linear, w4.w4a16_geglu_linear_prepacked) if geglu
+              else (w4.w4a16_linear, w4.w4a16_linear_prepacked))
+    y0 = f0(xd, q, s, bd)
+    y1 = f1(xd, w4.w4a16_prepack(q), s, bd)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(y1), bits(y0), f"prefill large grid prepacked vs row-major {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,f,k", [(65, 100, 256), (200, 300, 1024), (257, 64, 64)])

@@ -296,18 +296,38 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
                                         const void *scales, int64_t n_out, const void *bias,
                                         void *y, hipStream_t stream)
 {
-    // 128-token tiles (each dequantized operand feeds 8 MFMAs) unless the
-    // grid would leave the last wave of workgroups badly filled and the
-    // reduction is short: then 64-token tiles (measured: attention-out
-    // 12288 x 12288 at m = 2048, 1248 against 1054 TFLOP/s).
+    // Tile shape from the grid of the largest tile (4 x 16 x 4 rows x 128
+    // tokens; GeGLU 128 outputs x 128 tokens), measured at the GLM-130B
+    // widths for m = 128 ... 2048:
+    //  * a grid of at most about two such tiles per CU that does not fill
+    //    a whole wave of workgroups (two per CU) leaves CUs idle or thinly
+    //    used: the 192-row x 64-token tile (GeGLU: 64 outputs x 64 tokens,
+    //    at one large tile per CU or fewer) runs 4 workgroups per CU and
+    //    gives the most of them (FFN-down 12288 x 32768 at m = 128: 209
+    //    against 464 us; QKV 36864 x 12288 at m = 256: 210 against 275 us);
+    //    a grid that fills one wave exactly keeps the large tile (plain
+    //    FFN-up 65536 x 12288 at m = 256: 331 against 371 us);
+    //  * larger plain grids keep 128-token tiles unless they would fill the
+    //    last wave of workgroups much worse than 64-token tiles (k <= 16384);
+    //  * larger GeGLU grids take 128-token tiles.
     constexpr int out_per = 4 * 16 * (GEGLU ? 2 : 4);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
-    const int64_t slots = 2 * compute_units();
-    const double fill8 = wave_fill(tiles_n * ((m + 127) / 128), slots);
-    const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
-    if (k <= 16384 && fill4 > fill8 + 0.1)
-        return launch_prefill_t<4, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
-    return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    const int64_t cus = compute_units();
+    const int64_t g48 = tiles_n * ((m + 127) / 128);
+    if constexpr (GEGLU) {
+        if (g48 <= cus)
+            return launch_prefill_t<2, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    } else {
+        const int64_t slots = 2 * cus;
+        const double fill8 = wave_fill(g48, slots);
+        if (4 * g48 <= 9 * cus && fill8 < 0.9)
+            return launch_prefill_t<3, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+        const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
+        if (k <= 16384 && fill4 > fill8 + 0.1)
+            return launch_prefill_t<4, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+    }
 }
 
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
