@@ -20,7 +20,7 @@ The same JSON line also carries, measured in the same run:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   extra         GeGLU decode (fused up-projection, down-projection),
                 prefill GEMM TFLOP/s (attention-out and fused FFN-up at
-                M = 2048) against the 2.5 PFLOP/s fp16 MFMA peak, the
+                M = 2048 and 512) against the 2.5 PFLOP/s fp16 MFMA peak, the
                 quantizer, and the full 70-layer decode step at M = 8.
 Inputs are synthetic, seeded and resident in HBM before timing starts.
 """
@@ -331,6 +331,28 @@ def extra_workloads(torch, w4, synth, dev, a):
     del wf, yt
     res["prefill_m2048"] = pf
     log(f"prefill: {pf}")
+
+    # prefill at M = 512 (the short end of the prefill range): attention-out
+    # and the fused FFN-up, prepacked, with torch's fp16 GEMM as context
+    M5 = 512
+    x5 = synth.activations(M5, H, g, dev)
+    pf5 = {}
+    y5 = torch.empty(M5, H, dtype=torch.float16, device=dev)
+    pf5["attn_out"] = rec(time_launches(
+        torch, lambda: w4.w4a16_linear_prepacked(x5, attn[0][2], attn[0][1], y_out=y5), 20),
+        2.0 * M5 * H * H)
+    wf = synth.weight(H, H, g, device=dev)
+    t = time_launches(torch, lambda: torch.matmul(x5, wf.t(), out=y5), 20)
+    pf5["context_torch_fp16_matmul_attn_out"] = {"us": round(t * 1e6, 1),
+                                                 "TFLOPs": round(2.0 * M5 * H * H / t / 1e12, 1)}
+    del wf, y5
+    y6 = torch.empty(M5, F, dtype=torch.float16, device=dev)
+    pf5["ffn_up_geglu"] = rec(time_launches(
+        torch, lambda: w4.w4a16_geglu_linear_prepacked(x5, ups[0][2], ups[0][1], y_out=y6), 10),
+        2.0 * M5 * 2 * F * H)
+    del y6, x5
+    res["prefill_m512"] = pf5
+    log(f"prefill M=512: {pf5}")
     del ups, attn
 
     # quantizer: QKV-shaped fp16 weight -> packed + scales
