@@ -98,8 +98,9 @@ w4a16_status quantize_rowwise_int4(const void *w_fp16, int64_t n, int64_t k,
  *   bias_fp16   in   fp16  [n] or NULL
  *   y_fp16      out  fp16  [m][n]
  *
- * m <= 64 runs the memory-bound decode kernel; larger m the MFMA GEMM.
- * Results are deterministic (no atomics, fixed reduction order).
+ * m <= 64 runs the memory-bound decode kernel, 64 < m <= 128 runs it twice
+ * (tokens 0..63, then the rest), larger m runs the MFMA GEMM.  Results are
+ * deterministic (no atomics, fixed reduction order).
  */
 w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k,
                           const void *q_packed, const void *scales_fp16, int64_t n,

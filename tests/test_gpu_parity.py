@@ -241,6 +241,35 @@ def test_decode_every_launch_class(n, k):
         assert_bits_equal(bits(y1), bits(y0), f"class prepacked vs row-major {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m", [65, 100, 128])
+def test_two_decode_launches(m):
+    """64 < m <= 128 runs the decode kernel on tokens 0..63, then on the
+    rest through offset activation and output pointers.  Against the
+    oracle (ragged n and k, bias, plain and GeGLU), bit-identical in both
+    layouts and to separate calls on the two token ranges."""
+    g = synth.generator(2300 + m)
+    for geglu, rows, k in ((False, 1000, 1120), (True, 2 * 496, 1056)):
+        w = synth.weight(rows, k, g, "t4")
+        bias = synth.normal_fp16((rows,), 0.5, g)
+        q, s, p_ref, s_ref = quantize_both(w, f"two launches rows={rows}")
+        x = synth.activations(m, k, g)
+        if geglu:
+            check_geglu(x, q, s, p_ref, s_ref, f"two launches geglu m={m}", bias)
+            f0, f1 = w4.w4a16_geglu_linear, w4.w4a16_geglu_linear_prepacked
+        else:
+            check_linear(x, q, s, p_ref, s_ref, f"two launches m={m}", bias)
+            f0, f1 = w4.w4a16_linear, w4.w4a16_linear_prepacked
+        announce("two launches split", m, rows, k, geglu)
+        xd, bd = x.to(DEV), bias.to(DEV)
+        y = f0(xd, q, s, bd)
+        yp = f1(xd, w4.w4a16_prepack(q), s, bd)
+        lo = f0(xd[:64].contiguous(), q, s, bd)
+        hi = f0(xd[64:].contiguous(), q, s, bd)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(yp), bits(y), f"two launches prepacked vs row-major m={m} geglu={geglu}")
+        assert_bits_equal(bits(y), np.concatenate([bits(lo), bits(hi)]), f"two launches vs split calls m={m}")
+
+
 @pytest.mark.parametrize("n", [1001, 1002, 1003])
 def test_decode_rows_not_a_multiple_of_four(n):
     """Output rows of n values lose 8-byte alignment when n % 4 != 0: every

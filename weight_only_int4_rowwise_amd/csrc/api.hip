@@ -89,10 +89,25 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
         return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (m <= kDecodeMaxM)
+    if (m <= kDecodeMaxM) {
         e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
-    else
+    } else if (m <= 2 * kDecodeMaxM) {
+        // 64 < m <= 128: the first 64 tokens, then the rest, each through
+        // the decode kernel.  The weights stream twice, but every CU stays
+        // busy, where the GEMM's tiles leave most of the chip idle at this
+        // size (FFN-down 12288 x 32768 at m = 65: 122 against 207 us;
+        // attention-out 12288 x 12288 at m = 96: 59 against 83 us).
+        // Outputs depend only on their own token row, so the split changes
+        // no result bits.
+        e = w4a16::launch_decode(x, (int)kDecodeMaxM, k, q, s, n_out, bias, y, geglu, tiled, hs);
+        if (e == hipSuccess)
+            e = w4a16::launch_decode(static_cast<const uint16_t *>(x) + kDecodeMaxM * k,
+                                     (int)(m - kDecodeMaxM), k, q, s, n_out, bias,
+                                     static_cast<uint16_t *>(y) + kDecodeMaxM * n_out, geglu,
+                                     tiled, hs);
+    } else {
         e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, hs);
+    }
     return from_hip(e);
 }
 
