@@ -107,9 +107,9 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     constexpr int KS = W / RG;
     constexpr int KC = 128 * KU;              // reduction indices per chunk
     constexpr int RP = KC / 8;                // 16-byte pieces per activation row per chunk
-    // Several token blocks: activations by LDS DMA into XOR-swizzled rows.
-    // One block: through registers into padded rows (measured faster there).
-    constexpr bool XDMA = MB > 1;
+    // 16 or more token rows: activations by LDS DMA into XOR-swizzled rows.
+    // 4 or 8 rows: through registers into padded rows (measured faster there).
+    constexpr bool XDMA = MR >= 16;
     constexpr int LD = XDMA ? KC : KC + 8;    // row stride (halves)
     constexpr int SLOT = MR * LD * 2;         // bytes of one chunk slot (MR rows)
     constexpr int STAGE = KS * SLOT;          // bytes of one round's activations
