@@ -1,4 +1,5 @@
-// Decode W4A16 GEMV / skinny GEMM (m <= 64) for gfx950.
+// Decode W4A16 GEMV / skinny GEMM (m <= 64 tokens per launch; the library
+// runs it twice for 64 < m <= 128) for gfx950.
 //
 // y[i][r] = fp16(s[r] * sum_c x[i][c] * q[r][c] + bias[r])   (GLM-130B paper
 // card, "Method": linear_forward with the weights turned back into FP16 at
