@@ -3,8 +3,9 @@ benchmark times.
 
 Inputs are drawn on the GPU (seeded ``torch.Generator('cuda')``; the same
 tensors are copied to the host for the oracle).  Quantized bytes and scales
-are compared in full; decode outputs (m <= 64) in full; prefill outputs
-(m = 2048) on sampled rows and columns that touch every output tile.
+are compared in full; decode outputs (m <= 64) in full; two-launch decode
+(m = 100) and prefill outputs (m = 512, 2048) on sampled rows and columns
+that touch every output tile.
 """
 import numpy as np
 import pytest
@@ -59,6 +60,22 @@ def test_qkv_decode_full(qkv, m):
     y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
     r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
     print(f"QKV M={m}: max err/bound {r:.4f}")
+
+
+def test_qkv_two_decode_launches_sampled(qkv):
+    """64 < m <= 128 runs the decode kernel on tokens 0..63, then on the
+    rest: QKV at m = 100, one token in every 16-token block and two
+    columns in every 144-row workgroup tile, against the oracle."""
+    q, s, p_ref, s_ref, _ = qkv
+    m = 100
+    x = synth.activations(m, synth.HIDDEN, synth.generator(7, DEV), DEV)
+    announce("QKV two decode launches", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(m, q.shape[0], 16, 144, 5)
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
+    print(f"QKV M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
 @pytest.fixture(scope="module")
@@ -132,6 +149,21 @@ def test_prefill_attn_out_sampled(prefill_data):
     yg = _gather(y, mi, ni)
     r = assert_within(yg, y_ref, oracle.linear_bound(mag), "prefill attn-out")
     print(f"prefill attn-out: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
+def test_prefill_attn_out_m512_sampled(prefill_data):
+    """m = 512 runs the small-grid tiles (192 rows x 64 tokens) on the
+    attention-out weight: one token in every 64-token tile and two columns
+    in every 192-row tile."""
+    (q, s, p_ref, s_ref), _, x = prefill_data
+    x5 = x[:512].contiguous()
+    announce("prefill attn-out", tuple(x5.shape))
+    y = w4.w4a16_linear(x5, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(x5.shape[0], q.shape[0], 64, 192, 6)
+    y_ref, mag = oracle.linear_at(bits(x5), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "prefill attn-out m=512")
+    print(f"prefill attn-out m=512: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
 def test_prefill_ffn_up_geglu_sampled(prefill_data):
