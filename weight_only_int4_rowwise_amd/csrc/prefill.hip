@@ -57,7 +57,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kStepBytes];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    // uniform: the DMA destinations and row offsets stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane % 16;
     const int g = lane / 16;
 
