@@ -31,6 +31,31 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
+// Four consecutive fp16 values p[o .. o + 3] (o a multiple of 4), packed
+// two per word (0 for no p); entries at or past `count` repeat entry
+// count - 1 (their outputs are never stored).  `whole` says that p is 8-byte
+// aligned, a fact about the whole call: then one 8-byte load serves when all
+// four are in range.
+__device__ __forceinline__ uint2 load4_h(const uint16_t *__restrict__ p, int o, int count, bool whole)
+{
+    if (!p)
+        return uint2{0u, 0u};
+    if (whole && o + 3 < count)
+        return *reinterpret_cast<const uint2 *>(p + o);
+    uint32_t h[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        h[c] = p[o + c < count ? o + c : count - 1];
+    return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// Entry i (0..3) of four packed fp16 values, as a float.
+__device__ __forceinline__ float half4_at(uint2 v, int i)
+{
+    const uint32_t w = i < 2 ? v.x : v.y;
+    return half_bits_to_float((uint16_t)((i & 1) ? w >> 16 : w & 0xFFFFu));
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel (m <= 64).
 //
@@ -66,31 +91,6 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b)
 // wavefront reads KU KB of consecutive memory per chunk and row group
 // instead of 16 row segments of 64 KU bytes.
 // ---------------------------------------------------------------------------
-// Four consecutive fp16 values p[o .. o + 3] (o a multiple of 4), packed
-// two per word (0 for no p); entries at or past `count` repeat entry
-// count - 1 (their outputs are never stored).  `whole` says that p is 8-byte
-// aligned, a fact about the whole call: then one 8-byte load serves when all
-// four are in range.
-__device__ __forceinline__ uint2 load4_h(const uint16_t *__restrict__ p, int o, int count, bool whole)
-{
-    if (!p)
-        return uint2{0u, 0u};
-    if (whole && o + 3 < count)
-        return *reinterpret_cast<const uint2 *>(p + o);
-    uint32_t h[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        h[c] = p[o + c < count ? o + c : count - 1];
-    return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-}
-
-// Entry i (0..3) of four packed fp16 values, as a float.
-__device__ __forceinline__ float half4_at(uint2 v, int i)
-{
-    const uint32_t w = i < 2 ? v.x : v.y;
-    return half_bits_to_float((uint16_t)((i & 1) ? w >> 16 : w & 0xFFFFu));
-}
-
 template <int MB, int MR>
 struct TokenTile {
     static_assert(MB == 1 ? (MR == 4 || MR == 8 || MR == 16) : MR == 16 * MB, "token rows");
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     //    8 P + 7 of the chunk) of row r is stored at piece P ^ (r mod 16), so
     //    the 16 rows an MFMA B-operand read touches start at different
     //    banks.  DMA load i of this wave is the round's 1 KB load c = wave +
-    //    4 i; lane l fills 16-byte unit 64 c + l (whole row segments, so a
+    //    W i; lane l fills 16-byte unit 64 c + l (whole row segments, so a
     //    load covers few cache lines).
     //  * otherwise: each thread loads pieces into registers at the top of a
     //    round and stores them into rows padded by 16 bytes at its end.
