@@ -304,8 +304,8 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //    a whole wave of workgroups (two per CU) leaves CUs idle or thinly
     //    used: the 192-row x 64-token tile (GeGLU: 64 outputs x 64 tokens,
     //    at one large tile per CU or fewer) runs 4 workgroups per CU and
-    //    gives the most of them (FFN-down 12288 x 32768 at m = 128: 209
-    //    against 464 us; QKV 36864 x 12288 at m = 256: 210 against 275 us);
+    //    gives the most of them (FFN-down 12288 x 32768 at m = 256: 235
+    //    against 467 us; QKV 36864 x 12288 at m = 256: 207 against 282 us);
     //    a grid that fills one wave exactly keeps the large tile (plain
     //    FFN-up 65536 x 12288 at m = 256: 331 against 371 us);
     //  * larger plain grids keep 128-token tiles unless they would fill the
