@@ -112,6 +112,40 @@ def test_down_decode_full(ffn, m):
     print(f"down M={m}: max err/bound {r:.4f}")
 
 
+# 4-way tensor-parallel shards of the GLM-130B linears, the layout the pages
+# serve INT4 with (paper card, "Paper vs code"): QKV and FFN-up split their
+# output rows, attention-out and FFN-down their reduction.
+_SHARDS = {"qkv/4": (9216, 12288, False, "normal"), "attn_out/4": (12288, 3072, False, "normal"),
+           "down/4": (12288, 8192, False, "t4"), "up_geglu/4": (8192, 12288, True, "t4")}
+
+
+@pytest.mark.parametrize("name", list(_SHARDS))
+def test_tensor_parallel_shard_decode(name):
+    """Decode on one GPU's shard at m = 1, 8, 32, 48 (prepacked weights),
+    every output against the oracle."""
+    n, k, geglu, dist = _SHARDS[name]
+    rows = 2 * n if geglu else n
+    g = synth.generator(3100 + rows + k, DEV)
+    w = synth.weight(rows, k, g, dist, device=DEV)
+    q, s, p_ref, s_ref = _quantize_checked(w, f"shard {name} {rows}x{k}")
+    del w
+    qp = w4.w4a16_prepack(q)
+    for m in (1, 8, 32, 48):
+        x = synth.activations(m, k, g, DEV)
+        announce("shard decode", name, m)
+        if geglu:
+            y = w4.w4a16_geglu_linear_prepacked(x, qp, s)
+            torch.cuda.synchronize()
+            gr, a, b, ma, mb = oracle.geglu(bits(x), p_ref, s_ref)
+            r = assert_within(f64(y), gr, oracle.geglu_bound(gr, a, b, ma, mb), f"shard {name} M={m}")
+        else:
+            y = w4.w4a16_linear_prepacked(x, qp, s)
+            torch.cuda.synchronize()
+            y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
+            r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"shard {name} M={m}")
+        print(f"shard {name} M={m}: max err/bound {r:.4f}")
+
+
 def _gather(y, mi, ni):
     """y[mi[t], ni[t]] taken on the device (the full output is large)."""
     return y[torch.as_tensor(mi, device=y.device), torch.as_tensor(ni, device=y.device)].double().cpu().numpy()

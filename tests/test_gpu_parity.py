@@ -214,16 +214,19 @@ def test_geglu_fused_matches_unfused_halves():
 
 
 # ------------------------------------------------ every decode launch class
-# The decode launch shape depends on the token class (m <= 1, 4, 8, 16, 32,
-# 48, 64) and on the weight height (under 24576 rows, under 49152, more).
-# One weight per height class, every token class, a reduction length that
-# is a whole number of rounds for every shape of that class (the
-# instantiations without per-index checks), and both weight layouts.
+# The decode launch shape depends on the token class (m <= 4, 8, 16, 32, 48,
+# 64), on the weight height (plain: bands from 8192, 16384, 24576 and 49152
+# rows; GeGLU: from 12288, 24576 and 49152 rows of both halves) and, for
+# 8192 to 16383 rows, on whether the reduction is short (k below or at
+# 4096).  One weight per band (and both sides of the reduction threshold),
+# every token class, reduction lengths that are whole and partial rounds of
+# the chosen shapes, and both weight layouts.
 
 _CLASS_MS = [1, 3, 8, 12, 17, 32, 45, 64]
 
 
-@pytest.mark.parametrize("n,k", [(1000, 2048), (36848, 1024), (65520, 1024)])
+@pytest.mark.parametrize("n,k", [(1000, 2048), (8200, 4160), (12280, 1024), (12288, 4096),
+                                 (18424, 1024), (36848, 1024), (65520, 1024)])
 def test_decode_every_launch_class(n, k):
     g = synth.generator(1800 + n)
     w = synth.weight(n, k, g, "t4")
@@ -305,7 +308,7 @@ def test_decode_geglu_halves_not_a_multiple_of_four(f):
         check_geglu(x, q, s, p_ref, s_ref, f"geglu f%4 {m}x{f}x{k} bias", bias)
 
 
-@pytest.mark.parametrize("f,k", [(496, 2048), (32752, 1024)])
+@pytest.mark.parametrize("f,k", [(496, 2048), (6160, 1024), (12304, 1024), (32752, 1024)])
 def test_decode_geglu_every_launch_class(f, k):
     g = synth.generator(1900 + f)
     w = synth.weight(2 * f, k, g, "t4")

@@ -474,60 +474,96 @@ void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const 
 
 // Launch shapes per token class and weight height (rows = n, or 2 f for
 // GeGLU), from sweeps over KU, RG, W, D and NGW on MI355X at the GLM-130B
-// shapes (12288, 36864 and 65536 rows; 12288 and 32768 columns).  Each
-// workgroup reads the activations once for all its rows, so tall matrices
-// want many rows per workgroup, spread over more wavefronts (W up to 16)
-// rather than more row groups per wavefront (which costs registers and
-// occupancy); for the 36864-row QKV projection, 144 rows per workgroup
-// (3 row sets x 4 K-parts, 12 wavefronts) make exactly one workgroup per
-// CU.  Short matrices want more reduction splits (more wavefronts per
-// row), and more token blocks want more row groups per wavefront (each
-// activation operand feeds more MFMAs).  At m > 48 tall weights keep three
-// weight register sets in flight (D = 3): the round there is long enough
-// that two sets leave the wave waiting on the loads.
+// shapes (12288, 36864 and 65536 rows; 12288 and 32768 columns) and at
+// their 2-, 4- and 8-way tensor-parallel shards (4608 to 32768 rows, 1536
+// to 16384 columns).  Each workgroup reads the activations once for all its
+// rows, so tall matrices want many rows per workgroup, spread over more
+// wavefronts (W up to 16) rather than more row groups per wavefront (which
+// costs registers and occupancy); for the 36864-row QKV projection, 144 rows
+// per workgroup (3 row sets x 4 K-parts, 12 wavefronts) make exactly one
+// workgroup per CU.  Shorter matrices want fewer rows per workgroup, so that
+// the grid still covers the 256 CUs (below about 8192 rows: 16 or 32 rows),
+// and more reduction splits (more wavefronts per row); a short reduction
+// (k <= 4096) wants a short round (128 or 256 columns per K-part), or the
+// ring never fills.  More token blocks want more row groups per wavefront
+// (each activation operand feeds more MFMAs).  At m > 48 tall weights keep
+// three weight register sets in flight (D = 3): the round there is long
+// enough that two sets leave the wave waiting on the loads.
 template <bool GEGLU, bool TILED>
 static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const void *packed,
                                        const void *scales, int64_t n_out, const void *bias, void *y,
                                        hipStream_t stream)
 {
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
-    const int tall = rows >= 49152 ? 2 : rows >= 24576 ? 1 : 0;
 #define W4_DEC(KU, RG, W, D, MB, MR, NGW)                                                         \
     launch_decode_e<KU, RG, W, D, MB, MR, NGW, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, \
                                                              y, stream)
     if constexpr (GEGLU) {
-        // a wavefront always holds gate and value groups: NGW even
+        // a wavefront always holds gate and value groups: NGW even.
+        // Height bands: 3 from 49152 rows, 2 from 24576, 1 from 12288, 0 below.
+        const int b = rows >= 49152 ? 3 : rows >= 24576 ? 2 : rows >= 12288 ? 1 : 0;
         if (m <= 4)
-            tall == 2 ? W4_DEC(2, 4, 8, 2, 1, 4, 2) : W4_DEC(2, 2, 4, 2, 1, 4, 2);
+            b == 3   ? W4_DEC(2, 4, 8, 2, 1, 4, 2)
+            : b == 2 ? W4_DEC(2, 2, 4, 2, 1, 4, 2)
+            : b == 1 ? W4_DEC(2, 1, 4, 2, 1, 4, 2)
+                     : W4_DEC(2, 1, 8, 2, 1, 4, 2);
         else if (m <= 8)
-            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 8, 2) : W4_DEC(4, 2, 4, 2, 1, 8, 2);
+            b == 3 ? W4_DEC(2, 4, 4, 2, 1, 8, 2)
+            : b    ? W4_DEC(2, 2, 8, 2, 1, 8, 2)
+                   : W4_DEC(2, 1, 8, 2, 1, 8, 2);
         else if (m <= 16)
-            tall == 2 ? W4_DEC(2, 8, 16, 2, 1, 16, 2) : W4_DEC(4, 2, 4, 2, 1, 16, 2);
+            b == 3 ? W4_DEC(2, 8, 16, 2, 1, 16, 2)
+            : b    ? W4_DEC(2, 2, 8, 2, 1, 16, 2)
+                   : W4_DEC(2, 1, 8, 2, 1, 16, 2);
         else if (m <= 32)
-            tall == 2 ? W4_DEC(1, 4, 16, 2, 2, 32, 4) : W4_DEC(2, 2, 4, 2, 2, 32, 4);
+            b == 3   ? W4_DEC(1, 4, 16, 2, 2, 32, 4)
+            : b == 2 ? W4_DEC(2, 2, 4, 2, 2, 32, 4)
+            : b == 1 ? W4_DEC(2, 2, 8, 2, 2, 32, 2)
+                     : W4_DEC(2, 1, 4, 2, 2, 32, 2);
         else if (m <= 48)
-            tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4) : W4_DEC(1, 2, 4, 2, 3, 48, 4);
+            b == 3   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
+            : b == 2 ? W4_DEC(1, 2, 4, 2, 3, 48, 4)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 4)
+                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
         else
-            tall == 2 ? W4_DEC(1, 8, 16, 3, 4, 64, 2) : W4_DEC(2, 2, 4, 2, 4, 64, 2);
+            b == 3 ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
+            : b    ? W4_DEC(2, 2, 4, 2, 4, 64, 2)
+                   : W4_DEC(1, 1, 4, 2, 4, 64, 2);
     } else {
+        // Height bands: 4 from 49152 rows, 3 from 24576, 2 from 16384,
+        // 1 from 8192, 0 below.
+        const int b = rows >= 49152 ? 4 : rows >= 24576 ? 3 : rows >= 16384 ? 2 : rows >= 8192 ? 1 : 0;
         if (m <= 4)
-            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 4, 1)
-                      : tall ? W4_DEC(2, 3, 6, 2, 1, 4, 1) : W4_DEC(2, 1, 4, 2, 1, 4, 1);
+            b == 4   ? W4_DEC(2, 4, 4, 2, 1, 4, 1)
+            : b == 3 ? W4_DEC(2, 3, 6, 2, 1, 4, 1)
+            : b      ? W4_DEC(2, 1, 4, 2, 1, 4, 1)
+                     : W4_DEC(2, 1, 8, 2, 1, 4, 1);
         else if (m <= 8)
-            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 8, 1)
-                      : tall ? W4_DEC(1, 1, 4, 2, 1, 8, 3) : W4_DEC(4, 3, 12, 2, 1, 8, 1);
+            b == 4   ? W4_DEC(2, 4, 4, 2, 1, 8, 1)
+            : b >= 2 ? W4_DEC(1, 1, 4, 2, 1, 8, 3)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 1, 4, 2, 1, 8, 1) : W4_DEC(4, 3, 12, 2, 1, 8, 1))
+                     : W4_DEC(2, 2, 8, 2, 1, 8, 1);
         else if (m <= 16)
-            tall == 2 ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
-                      : tall ? W4_DEC(2, 3, 12, 2, 1, 16, 3) : W4_DEC(2, 1, 8, 2, 1, 16, 3);
+            b == 4                  ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
+            : b == 3                ? W4_DEC(2, 3, 12, 2, 1, 16, 3)
+            : b == 2 || (b == 1 && k < 4096) ? W4_DEC(1, 1, 4, 2, 1, 16, 3)
+            : b == 1                ? W4_DEC(2, 1, 8, 2, 1, 16, 3)
+                                    : W4_DEC(2, 2, 8, 2, 1, 16, 1);
         else if (m <= 32)
-            tall == 2 ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
-                      : tall ? W4_DEC(2, 3, 12, 2, 2, 32, 3) : W4_DEC(2, 1, 4, 2, 2, 32, 3);
+            b == 4   ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
+            : b >= 2 ? W4_DEC(2, 3, 12, 2, 2, 32, 3)
+            : b == 1 ? (k <= 4096 ? W4_DEC(1, 2, 8, 2, 2, 32, 2) : W4_DEC(2, 1, 4, 2, 2, 32, 3))
+                     : W4_DEC(2, 1, 4, 2, 2, 32, 2);
         else if (m <= 48)
-            tall == 2 ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
-                      : tall ? W4_DEC(1, 3, 12, 2, 3, 48, 3) : W4_DEC(1, 1, 4, 2, 3, 48, 3);
+            b == 4   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
+            : b >= 2 ? W4_DEC(1, 3, 12, 2, 3, 48, 3)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 3)
+                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
         else
-            tall == 2 ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
-                      : tall ? W4_DEC(1, 3, 12, 3, 4, 64, 3) : W4_DEC(1, 1, 4, 2, 4, 64, 3);
+            b == 4   ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
+            : b >= 2 ? W4_DEC(1, 3, 12, 3, 4, 64, 3)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 4, 64, 3)
+                     : W4_DEC(1, 1, 4, 2, 4, 64, 2);
     }
 #undef W4_DEC
     return hipGetLastError();
