@@ -38,9 +38,15 @@ def library():
     return _lib.load()
 
 
+_torch_mod = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _require(t, dtype, name):
@@ -55,9 +61,45 @@ def _require(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream_ptr(device):
+def _same_device(t, dev, name, what):
+    if t.get_device() != dev:
+        raise ValueError(f"{what}: {name} on {t.device}, expected cuda:{dev}")
+
+
+_stream_getter = None
+
+
+def _raw_stream(dev):
+    """Handle of the current stream of GPU `dev` (torch's current stream):
+    torch's raw-handle query where it has one, else the Stream object's."""
+    global _stream_getter
+    if _stream_getter is None:
+        torch = _torch()
+        _stream_getter = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+            (lambda d: torch.cuda.current_stream(d).cuda_stream)
+    return _stream_getter(dev)
+
+
+def _launch(fn, dev, *args):
+    """fn(*args, stream) with GPU `dev` current and its current stream."""
     torch = _torch()
-    return torch.cuda.current_stream(device).cuda_stream
+    if torch.cuda.current_device() == dev:
+        return fn(*args, _raw_stream(dev))
+    with torch.cuda.device(dev):
+        return fn(*args, _raw_stream(dev))
+
+
+_PREPACKED_SIZES: dict = {}
+
+
+def _prepacked_size(lib, rows, k):
+    """w4a16_prepacked_bytes(rows, k), remembered per shape."""
+    key = (rows, k)
+    size = _PREPACKED_SIZES.get(key)
+    if size is None:
+        size = int(lib.w4a16_prepacked_bytes(rows, k))
+        _PREPACKED_SIZES[key] = size
+    return size
 
 
 def quantize_rowwise_int4(w, q_out=None, s_out=None):
@@ -76,9 +118,8 @@ def quantize_rowwise_int4(w, q_out=None, s_out=None):
     _require(s_out, torch.float16, "s_out")
     if tuple(q_out.shape) != (n, k // 2) or tuple(s_out.shape) != (n,):
         raise ValueError("output shape mismatch")
-    with torch.cuda.device(w.device):
-        st = lib.quantize_rowwise_int4(w.data_ptr(), n, k, q_out.data_ptr(), s_out.data_ptr(),
-                                       _stream_ptr(w.device))
+    st = _launch(lib.quantize_rowwise_int4, w.get_device(),
+                 w.data_ptr(), n, k, q_out.data_ptr(), s_out.data_ptr())
     _lib.check(st, "quantize_rowwise_int4")
     return q_out, s_out
 
@@ -93,18 +134,20 @@ def _linear_common(x, q, s, bias, out_cols, rows, y_out, name):
     m, k = x.shape
     if q.shape[0] != rows or q.shape[1] * 2 != k or s.shape[0] != rows:
         raise ValueError(f"{name}: shape mismatch x {tuple(x.shape)} q {tuple(q.shape)} s {tuple(s.shape)}")
-    for t, nm in ((q, "q"), (s, "s")):
-        if t.device != x.device:
-            raise ValueError(f"{name}: {nm} on {t.device}, x on {x.device}")
+    dev = x.get_device()
+    _same_device(q, dev, "q", name)
+    _same_device(s, dev, "s", name)
     if bias is not None:
         _require(bias, torch.float16, "bias")
-        if tuple(bias.shape) != (rows,) or bias.device != x.device:
-            raise ValueError(f"{name}: bias must be fp16 [{rows}] on {x.device}")
+        if tuple(bias.shape) != (rows,):
+            raise ValueError(f"{name}: bias must be fp16 [{rows}]")
+        _same_device(bias, dev, "bias", name)
     if y_out is None:
         y_out = torch.empty((m, out_cols), dtype=torch.float16, device=x.device)
     _require(y_out, torch.float16, "y_out")
     if tuple(y_out.shape) != (m, out_cols):
         raise ValueError(f"{name}: y_out must be [{m}][{out_cols}]")
+    _same_device(y_out, dev, "y_out", name)
     return m, k, y_out
 
 
@@ -113,11 +156,9 @@ def w4a16_linear(x, q, s, bias=None, y_out=None):
     lib = _lib.load()
     n = q.shape[0]
     m, k, y_out = _linear_common(x, q, s, bias, n, n, y_out, "w4a16_linear")
-    torch = _torch()
-    with torch.cuda.device(x.device):
-        st = lib.w4a16_linear(x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), n,
-                              None if bias is None else bias.data_ptr(), y_out.data_ptr(),
-                              _stream_ptr(x.device))
+    st = _launch(lib.w4a16_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_linear")
     return y_out
 
@@ -130,11 +171,9 @@ def w4a16_geglu_linear(x, q, s, bias=None, y_out=None):
         raise ValueError("w4a16_geglu_linear: q must have an even number of rows (2f)")
     f = rows // 2
     m, k, y_out = _linear_common(x, q, s, bias, f, rows, y_out, "w4a16_geglu_linear")
-    torch = _torch()
-    with torch.cuda.device(x.device):
-        st = lib.w4a16_geglu_linear(x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), f,
-                                    None if bias is None else bias.data_ptr(), y_out.data_ptr(),
-                                    _stream_ptr(x.device))
+    st = _launch(lib.w4a16_geglu_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_geglu_linear")
     return y_out
 
@@ -160,8 +199,7 @@ def w4a16_prepack(q, q_out=None):
     _require(q_out, torch.uint8, "q_out")
     if q_out.numel() != size or q_out.device != q.device:
         raise ValueError(f"w4a16_prepack: q_out must hold {size} bytes on {q.device}")
-    with torch.cuda.device(q.device):
-        st = lib.w4a16_prepack(q.data_ptr(), n, k, q_out.data_ptr(), _stream_ptr(q.device))
+    st = _launch(lib.w4a16_prepack, q.get_device(), q.data_ptr(), n, k, q_out.data_ptr())
     _lib.check(st, "w4a16_prepack")
     return q_out
 
@@ -175,49 +213,47 @@ def _prepacked_common(x, qp, s, bias, out_cols, rows, y_out, name):
     if x.dim() != 2 or s.dim() != 1 or s.shape[0] != rows:
         raise ValueError(f"{name}: x [m][k] and s [{rows}] expected")
     m, k = x.shape
-    size = lib.w4a16_prepacked_bytes(rows, k)
+    size = _prepacked_size(lib, rows, k)
     if size < 0 or qp.numel() != size:
         raise ValueError(f"{name}: prepacked weight must hold {size} bytes for {rows} x {k}")
-    for t, nm in ((qp, "qp"), (s, "s")):
-        if t.device != x.device:
-            raise ValueError(f"{name}: {nm} on {t.device}, x on {x.device}")
+    dev = x.get_device()
+    _same_device(qp, dev, "qp", name)
+    _same_device(s, dev, "s", name)
     if bias is not None:
         _require(bias, torch.float16, "bias")
-        if tuple(bias.shape) != (rows,) or bias.device != x.device:
-            raise ValueError(f"{name}: bias must be fp16 [{rows}] on {x.device}")
+        if tuple(bias.shape) != (rows,):
+            raise ValueError(f"{name}: bias must be fp16 [{rows}]")
+        _same_device(bias, dev, "bias", name)
     if y_out is None:
         y_out = torch.empty((m, out_cols), dtype=torch.float16, device=x.device)
     _require(y_out, torch.float16, "y_out")
     if tuple(y_out.shape) != (m, out_cols):
         raise ValueError(f"{name}: y_out must be [{m}][{out_cols}]")
+    _same_device(y_out, dev, "y_out", name)
     return lib, m, k, y_out
 
 
 def w4a16_linear_prepacked(x, qp, s, bias=None, y_out=None):
     """w4a16_linear with the weight in the prepacked layout (n = len(s))."""
-    torch = _torch()
     n = s.shape[0]
     lib, m, k, y_out = _prepacked_common(x, qp, s, bias, n, n, y_out, "w4a16_linear_prepacked")
-    with torch.cuda.device(x.device):
-        st = lib.w4a16_linear_prepacked(x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), n,
-                                        None if bias is None else bias.data_ptr(),
-                                        y_out.data_ptr(), _stream_ptr(x.device))
+    st = _launch(lib.w4a16_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_linear_prepacked")
     return y_out
 
 
 def w4a16_geglu_linear_prepacked(x, qp, s, bias=None, y_out=None):
     """w4a16_geglu_linear with the weight in the prepacked layout (f = len(s) / 2)."""
-    torch = _torch()
     rows = s.shape[0]
     if rows % 2:
         raise ValueError("w4a16_geglu_linear_prepacked: s must have 2f entries")
     f = rows // 2
     lib, m, k, y_out = _prepacked_common(x, qp, s, bias, f, rows, y_out,
                                          "w4a16_geglu_linear_prepacked")
-    with torch.cuda.device(x.device):
-        st = lib.w4a16_geglu_linear_prepacked(x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
-                                              None if bias is None else bias.data_ptr(),
-                                              y_out.data_ptr(), _stream_ptr(x.device))
+    st = _launch(lib.w4a16_geglu_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_geglu_linear_prepacked")
     return y_out
