@@ -367,19 +367,24 @@ def extra_workloads(torch, w4, synth, dev, a):
     del wq, qo, so
 
     if not a.no_full_step:
-        res["full_decode_step_m8"] = full_step(torch, w4, synth, dev)
+        res["full_decode_step_m8"] = full_step(torch, w4, synth, dev, synth.LAYER_LINEARS,
+                                               "full 70-layer decode step")
+        # one GPU's share of the model under 4-way tensor parallelism (the
+        # layout the pages serve INT4 with): the same step on the shard shapes
+        res["full_decode_step_m8_tp4_shard"] = full_step(torch, w4, synth, dev, synth.shard_linears(4),
+                                                         "70-layer decode step, 4-way shard")
     return res
 
 
-def full_step(torch, w4, synth, dev):
-    """70 layers x (QKV, attention-out, fused GeGLU up, down) at M = 8, all
-    weights resident (63.4 GB packed), launched back to back on one stream."""
-    log("full 70-layer decode step: generating and quantizing 280 matrices")
-    H, F = synth.HIDDEN, synth.FFN
+def full_step(torch, w4, synth, dev, linears, label):
+    """70 layers x the four linears of `linears` (name, rows, k) at M = 8,
+    all weights resident and prepacked, launched back to back on one
+    stream."""
+    log(f"{label}: generating and quantizing {synth.LAYERS * len(linears)} matrices")
     layers = []
     for l in range(synth.LAYERS):
         mats = []
-        for mid, (name, n, k) in enumerate(synth.LAYER_LINEARS):
+        for mid, (name, n, k) in enumerate(linears):
             g = synth.generator(synth.layer_weight_seed(l, mid), dev)
             w = synth.weight(n, k, g, device=dev)
             q, s = w4.quantize_rowwise_int4(w)
@@ -390,28 +395,27 @@ def full_step(torch, w4, synth, dev):
     torch.cuda.synchronize()
     g = synth.generator(7, dev)
     M = 8
-    xh = synth.activations(M, H, g, dev)
-    xf = synth.activations(M, F, g, dev)
-    y_qkv = torch.empty(M, synth.QKV_OUT, dtype=torch.float16, device=dev)
-    y_h = torch.empty(M, H, dtype=torch.float16, device=dev)
-    y_f = torch.empty(M, F, dtype=torch.float16, device=dev)
+    xs = {k: synth.activations(M, k, g, dev) for k in sorted({k for _, _, k in linears})}
+    calls = []
+    total = 0
+    for name, n, k in linears:
+        geglu = name == "ffn_up"
+        out = n // 2 if geglu else n
+        fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+        calls.append((fn, xs[k], torch.empty(M, out, dtype=torch.float16, device=dev)))
+        total += linear_bytes(M, n, k, out)
+    total *= synth.LAYERS
 
     def run():
         for mats in layers:
-            w4.w4a16_linear_prepacked(xh, mats[0][0], mats[0][1], y_out=y_qkv)
-            w4.w4a16_linear_prepacked(xh, mats[1][0], mats[1][1], y_out=y_h)
-            w4.w4a16_geglu_linear_prepacked(xh, mats[2][0], mats[2][1], y_out=y_f)
-            w4.w4a16_linear_prepacked(xf, mats[3][0], mats[3][1], y_out=y_h)
+            for (fn, x, y), (qp, s) in zip(calls, mats):
+                fn(x, qp, s, y_out=y)
 
     t = time_launches(torch, run, 3, warm=1)
-    total = 0
-    for name, n, k in synth.LAYER_LINEARS:
-        out = n // 2 if name == "ffn_up" else n
-        total += linear_bytes(M, n, k, out)
-    total *= synth.LAYERS
     r = {"ms": round(t * 1e3, 3), "bytes": total, "GBs": round(total / t / 1e9, 1),
-         "frac_hbm": round(total / t / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"full step: {r}")
+         "frac_hbm": round(total / t / 1e9 / HBM_PEAK_GBS, 4),
+         "shapes": [[name, n, k] for name, n, k in linears]}
+    log(f"{label}: {r}")
     del layers
     torch.cuda.empty_cache()
     return r

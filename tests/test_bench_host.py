@@ -43,3 +43,18 @@ def test_geglu_bytes_count_both_halves_of_the_weight():
 def test_source_hash_is_stable_and_short():
     h1, h2 = bench.csrc_hash(), bench.csrc_hash()
     assert h1 == h2 and len(h1) == 16 and int(h1, 16) >= 0
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_shard_linears_split_each_layer_evenly(tp):
+    """One GPU's shard of a layer: QKV and FFN-up split rows, attention-out
+    and down split the reduction; tp shards hold the whole layer."""
+    from weight_only_int4_rowwise_amd import synth
+    full = {name: (n, k) for name, n, k in synth.LAYER_LINEARS}
+    shard = {name: (n, k) for name, n, k in synth.shard_linears(tp)}
+    assert shard.keys() == full.keys()
+    for name, (n, k) in shard.items():
+        fn, fk = full[name]
+        assert n * k * tp == fn * fk
+        assert (n == fn // tp and k == fk) if name in ("qkv", "ffn_up") else (n == fn and k == fk // tp)
+    assert shard["ffn_up"][0] % 2 == 0

@@ -37,6 +37,19 @@ LAYER_LINEARS = (
 )
 
 
+def shard_linears(tp: int):
+    """The four linears of a layer as one GPU holds them under tp-way tensor
+    parallelism: QKV and the GeGLU up-projection split their output rows
+    (each GPU keeps a matching slice of gate and value rows, 2 F / tp rows
+    in all), attention-out and down split their reduction."""
+    return (
+        ("qkv", QKV_OUT // tp, HIDDEN),
+        ("attn_out", HIDDEN, HIDDEN // tp),
+        ("ffn_up", 2 * FFN // tp, HIDDEN),
+        ("ffn_down", HIDDEN, FFN // tp),
+    )
+
+
 def generator(seed: int = 0, device: str = "cpu") -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
