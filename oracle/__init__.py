@@ -1,4 +1,5 @@
-"""CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear.
+"""CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear,
+and for the INT8 row-wise variant (W8A16: divisor 127, one code per byte).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only users.  The GPU library never imports, links or
@@ -76,6 +77,11 @@ def _load():
         lib.oracle_linear_at.argtypes = [P, I, P, P, P, P, P, I, P, P]
         lib.oracle_geglu.argtypes = [P, I, I, P, P, I, P, P, P, P, P, P]
         lib.oracle_geglu_at.argtypes = [P, I, P, P, I, P, P, P, I, P, P, P, P, P]
+        lib.oracle_quantize_rowwise_int8.argtypes = [P, I, I, P, P]
+        lib.oracle_linear_int8.argtypes = [P, I, I, P, P, I, P, P, P]
+        lib.oracle_linear_int8_at.argtypes = [P, I, P, P, P, P, P, I, P, P]
+        lib.oracle_geglu_int8.argtypes = [P, I, I, P, P, I, P, P, P, P, P, P]
+        lib.oracle_geglu_int8_at.argtypes = [P, I, P, P, I, P, P, P, I, P, P, P, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -222,6 +228,97 @@ def geglu_at(x, packed, scales, mi, ni, bias=None):
     outs = [np.empty(mi.shape, dtype=np.float64) for _ in range(5)]
     _check(_load().oracle_geglu_at(_ptr(x), k, _ptr(packed), _ptr(scales), f, _ptr(b),
                                    _ptr(mi), _ptr(ni), mi.size, *[_ptr(o) for o in outs]))
+    return tuple(outs)
+
+
+# ------------------------------------------------------------ INT8 variant
+
+def quantize_rowwise_int8(w):
+    """W fp16 [n][k] -> (codes int8 [n][k], scale bits uint16 [n]); s = fp16(a/127)."""
+    w = _bits16(w)
+    n, k = w.shape
+    codes = np.empty((n, k), dtype=np.int8)
+    scales = np.empty(n, dtype=np.uint16)
+    _check(_load().oracle_quantize_rowwise_int8(_ptr(w), n, k, _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def _codes8(codes, k):
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    if codes.ndim != 2 or codes.shape[1] != k:
+        raise ValueError("INT8 codes must be [rows][k]")
+    return codes
+
+
+def linear_int8(x, codes, scales, bias=None):
+    """y = x . (s*q)^T (+ bias) over INT8 codes, binary64.  Returns (y, mag)."""
+    x = _bits16(x)
+    m, k = x.shape
+    codes = _codes8(codes, k)
+    scales = _bits16(scales)
+    n = codes.shape[0]
+    if scales.shape[0] != n:
+        raise ValueError("shape mismatch")
+    b = None if bias is None else _bits16(bias)
+    y = np.empty((m, n), dtype=np.float64)
+    mag = np.empty((m, n), dtype=np.float64)
+    _check(_load().oracle_linear_int8(_ptr(x), m, k, _ptr(codes), _ptr(scales), n,
+                                      _ptr(b), _ptr(y), _ptr(mag)))
+    return y, mag
+
+
+def linear_int8_at(x, codes, scales, mi, ni, bias=None):
+    """Selected outputs y[mi[t], ni[t]] over INT8 codes.  Returns (y, mag)."""
+    x = _bits16(x)
+    k = x.shape[1]
+    codes = _codes8(codes, k)
+    scales = _bits16(scales)
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    if mi.shape != ni.shape:
+        raise ValueError("index shape mismatch")
+    if mi.size and (mi.min() < 0 or mi.max() >= x.shape[0] or ni.min() < 0 or ni.max() >= codes.shape[0]):
+        raise IndexError("output index out of range")
+    b = None if bias is None else _bits16(bias)
+    y = np.empty(mi.shape, dtype=np.float64)
+    mag = np.empty(mi.shape, dtype=np.float64)
+    _check(_load().oracle_linear_int8_at(_ptr(x), k, _ptr(codes), _ptr(scales), _ptr(b),
+                                         _ptr(mi), _ptr(ni), mi.size, _ptr(y), _ptr(mag)))
+    return y, mag
+
+
+def geglu_int8(x, codes, scales, bias=None):
+    """GeGLU over INT8 codes [2f][k].  Returns (g, a, b, mag_a, mag_b)."""
+    x = _bits16(x)
+    m, k = x.shape
+    codes = _codes8(codes, k)
+    scales = _bits16(scales)
+    two_f = codes.shape[0]
+    if two_f % 2 or scales.shape[0] != two_f:
+        raise ValueError("shape mismatch")
+    f = two_f // 2
+    b = None if bias is None else _bits16(bias)
+    outs = [np.empty((m, f), dtype=np.float64) for _ in range(5)]
+    _check(_load().oracle_geglu_int8(_ptr(x), m, k, _ptr(codes), _ptr(scales), f, _ptr(b),
+                                     *[_ptr(o) for o in outs]))
+    return tuple(outs)
+
+
+def geglu_int8_at(x, codes, scales, mi, ni, bias=None):
+    """Selected GeGLU outputs over INT8 codes.  Returns (g, a, b, mag_a, mag_b)."""
+    x = _bits16(x)
+    k = x.shape[1]
+    codes = _codes8(codes, k)
+    scales = _bits16(scales)
+    f = codes.shape[0] // 2
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    if mi.size and (mi.min() < 0 or mi.max() >= x.shape[0] or ni.min() < 0 or ni.max() >= f):
+        raise IndexError("output index out of range")
+    b = None if bias is None else _bits16(bias)
+    outs = [np.empty(mi.shape, dtype=np.float64) for _ in range(5)]
+    _check(_load().oracle_geglu_int8_at(_ptr(x), k, _ptr(codes), _ptr(scales), f, _ptr(b),
+                                        _ptr(mi), _ptr(ni), mi.size, *[_ptr(o) for o in outs]))
     return tuple(outs)
 
 

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear.
+ * CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear,
+ * and for its INT8 row-wise variant (W8A16).
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only callers.  Nothing in the GPU
@@ -88,16 +89,17 @@ uint16_t oracle_double_to_half(double d)
 /* Quantization  [card-M] [card-PvC]                                       */
 /* ---------------------------------------------------------------------- */
 
-/* One output row.  Definition, in the pages' order:
+/* One output row with b-bit codes, qmax = 2^(b-1) - 1 (7 for INT4, 127 for
+ * INT8).  Definition, in the pages' order:
  *   a     = max_k |W[k]|                          (row absmax)
- *   s     = fp16(a / 7)                           (divisor 2^(b-1)-1 = 7, stored in FP16)
- *   q[k]  = clamp(round(W[k] / s), -7, 7)         (integers in [-7, 7])
+ *   s     = fp16(a / qmax)                        (divisor 2^(b-1)-1, stored in FP16)
+ *   q[k]  = clamp(round(W[k] / s), -qmax, qmax)   (integers in [-qmax, qmax])
  * Readings: round() is round-half-to-even on the exact real quotient (a
  * binary64 quotient of two binary16 values is never far enough from a
  * half-integer to be rounded across one, and exact ties are representable);
  * the codes are taken against the STORED fp16 scale; a row whose scale is 0
  * gets all-zero codes. */
-static int quantize_row(const uint16_t *w, int64_t k, int8_t *q, uint16_t *s_out)
+static int quantize_row_q(const uint16_t *w, int64_t k, double qmax, int8_t *q, uint16_t *s_out)
 {
     double a = 0.0;
     for (int64_t i = 0; i < k; ++i) {
@@ -107,21 +109,27 @@ static int quantize_row(const uint16_t *w, int64_t k, int8_t *q, uint16_t *s_out
         if (fabs(v) > a)
             a = fabs(v);
     }
-    uint16_t s_bits = oracle_double_to_half(a / 7.0);
+    uint16_t s_bits = oracle_double_to_half(a / qmax);
     double s = oracle_half_to_double(s_bits);
     for (int64_t i = 0; i < k; ++i) {
         double r = 0.0;
         if (s != 0.0) {
             r = nearbyint(oracle_half_to_double(w[i]) / s);
-            if (r > 7.0)
-                r = 7.0;
-            if (r < -7.0)
-                r = -7.0;
+            if (r > qmax)
+                r = qmax;
+            if (r < -qmax)
+                r = -qmax;
         }
         q[i] = (int8_t)r;   /* -0.0 becomes the integer 0 */
     }
     *s_out = s_bits;
     return ORACLE_OK;
+}
+
+/* b = 4: divisor and largest code 2^(b-1) - 1 = 7 [card-PvC]. */
+static int quantize_row(const uint16_t *w, int64_t k, int8_t *q, uint16_t *s_out)
+{
+    return quantize_row_q(w, k, 7.0, q, s_out);
 }
 
 /* Two codes per byte [card-M pseudocode comment, card-PvC "int8 packing"].
@@ -345,6 +353,137 @@ int oracle_geglu_at(const uint16_t *x, int64_t k, const uint8_t *packed,
                    bias ? bias + j : NULL, &a, &ma);
         linear_one(x + i * k, k, packed + (f + j) * (k / 2), scales[f + j],
                    bias ? bias + f + j : NULL, &b, &mb);
+        g[t] = oracle_gelu(a) * b;
+        if (a_out) a_out[t] = a;
+        if (b_out) b_out[t] = b;
+        if (mag_a) mag_a[t] = ma;
+        if (mag_b) mag_b[t] = mb;
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* INT8 row-wise variant (W8A16)                                           */
+/* [card-PvC] "Quantization scale": the scale of a b-bit code is the row's */
+/* absmax over 2^(b-1) - 1; for b = 8 that is 127, with codes in           */
+/* [-127, 127].  [card-H] reports INT8 weights next to INT4 and FP16.       */
+/* Readings as for INT4 (exact quotient, ties to even, codes against the   */
+/* stored fp16 scale, zero scale -> zero codes); storage is one two's-     */
+/* complement byte per code, layout [n][k], no packing.                    */
+/* ---------------------------------------------------------------------- */
+
+int oracle_quantize_rowwise_int8(const uint16_t *w, int64_t n, int64_t k,
+                                 int8_t *codes, uint16_t *scales)
+{
+    if (!w || !codes || !scales || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (check_fe())
+        return ORACLE_ERR_ROUNDING;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < n; ++r) {
+        int st = quantize_row_q(w + r * k, k, 127.0, codes + r * k, scales + r);
+        if (st) {
+#pragma omp atomic write
+            status = st;
+        }
+    }
+    return status;
+}
+
+/* One output of y = x . W_hat^T (+ bias), W_hat[n][k] = s[n] * q[n][k], with
+ * INT8 codes.  Every product x * s * q is exact in binary64 (11 + 11 + 7
+ * significant bits). */
+static void linear_one_i8(const uint16_t *xrow, int64_t k, const int8_t *qrow,
+                          uint16_t s_bits, const uint16_t *bias_n,
+                          double *y, double *mag)
+{
+    double s = oracle_half_to_double(s_bits);
+    double acc = 0.0, m = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double t = oracle_half_to_double(xrow[i]) * (s * (double)qrow[i]);
+        acc += t;
+        m += fabs(t);
+    }
+    if (bias_n) {
+        double b = oracle_half_to_double(*bias_n);
+        acc += b;
+        m += fabs(b);
+    }
+    *y = acc;
+    if (mag)
+        *mag = m;
+}
+
+int oracle_linear_int8(const uint16_t *x, int64_t m, int64_t k, const int8_t *codes,
+                       const uint16_t *scales, int64_t n, const uint16_t *bias,
+                       double *y, double *mag)
+{
+    if (!x || !codes || !scales || !y || m < 0 || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            linear_one_i8(x + i * k, k, codes + j * k, scales[j],
+                          bias ? bias + j : NULL, y + i * n + j, mag ? mag + i * n + j : NULL);
+    return ORACLE_OK;
+}
+
+int oracle_linear_int8_at(const uint16_t *x, int64_t k, const int8_t *codes,
+                          const uint16_t *scales, const uint16_t *bias,
+                          const int64_t *mi, const int64_t *ni, int64_t count,
+                          double *y, double *mag)
+{
+    if (!x || !codes || !scales || !mi || !ni || !y || count < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < count; ++t)
+        linear_one_i8(x + mi[t] * k, k, codes + ni[t] * k, scales[ni[t]],
+                      bias ? bias + ni[t] : NULL, y + t, mag ? mag + t : NULL);
+    return ORACLE_OK;
+}
+
+/* GeGLU over INT8 codes: rows [0, f) gated by GELU, rows [f, 2f) linear. */
+int oracle_geglu_int8(const uint16_t *x, int64_t m, int64_t k, const int8_t *codes,
+                      const uint16_t *scales, int64_t f, const uint16_t *bias,
+                      double *g, double *a_out, double *b_out,
+                      double *mag_a, double *mag_b)
+{
+    if (!x || !codes || !scales || !g || m < 0 || f < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < f; ++j) {
+            double a, b, ma, mb;
+            linear_one_i8(x + i * k, k, codes + j * k, scales[j],
+                          bias ? bias + j : NULL, &a, &ma);
+            linear_one_i8(x + i * k, k, codes + (f + j) * k, scales[f + j],
+                          bias ? bias + f + j : NULL, &b, &mb);
+            g[i * f + j] = oracle_gelu(a) * b;
+            if (a_out) a_out[i * f + j] = a;
+            if (b_out) b_out[i * f + j] = b;
+            if (mag_a) mag_a[i * f + j] = ma;
+            if (mag_b) mag_b[i * f + j] = mb;
+        }
+    return ORACLE_OK;
+}
+
+int oracle_geglu_int8_at(const uint16_t *x, int64_t k, const int8_t *codes,
+                         const uint16_t *scales, int64_t f, const uint16_t *bias,
+                         const int64_t *mi, const int64_t *ni, int64_t count,
+                         double *g, double *a_out, double *b_out,
+                         double *mag_a, double *mag_b)
+{
+    if (!x || !codes || !scales || !mi || !ni || !g || count < 0 || f < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < count; ++t) {
+        int64_t i = mi[t], j = ni[t];
+        double a, b, ma, mb;
+        linear_one_i8(x + i * k, k, codes + j * k, scales[j],
+                      bias ? bias + j : NULL, &a, &ma);
+        linear_one_i8(x + i * k, k, codes + (f + j) * k, scales[f + j],
+                      bias ? bias + f + j : NULL, &b, &mb);
         g[t] = oracle_gelu(a) * b;
         if (a_out) a_out[t] = a;
         if (b_out) b_out[t] = b;

@@ -293,3 +293,141 @@ def test_geglu_vs_numpy_halves(oracle_mod):
     mi = np.array([0, 2, 1]); ni = np.array([0, 47, 20])
     gs = oracle_mod.geglu_at(x, p, s, mi, ni)
     assert np.array_equal(gs[0], gg[mi, ni])
+
+
+# ---------------------------------------------------------- INT8 variant
+# Same scheme with b = 8: divisor and largest code 2^(b-1) - 1 = 127, one
+# two's-complement byte per code.
+
+def _nearest_code8(w: Fraction, s: Fraction, guess: int) -> int:
+    """argmin_j |w - s*j| over j in [-127, 127] (ties to the even j), searched
+    exactly in a window around a float estimate: if the true nearest code lay
+    outside the window, the search would return a different code and the
+    comparison would fail."""
+    best = None
+    for j in range(max(-127, guess - 3), min(127, guess + 3) + 1):
+        key = (abs(w - s * j), j & 1)
+        if best is None or key < best[0]:
+            best = (key, j)
+    return best[1]
+
+
+def test_int8_scale_exhaustive_over_all_absmax_values(oracle_mod):
+    """s = fp16(a/127) for every finite non-negative fp16 absmax a, against
+    an exact-rational nearest search."""
+    a = synth.all_finite_nonneg_fp16().numpy()
+    w = np.stack([a, np.zeros_like(a)], axis=1)
+    _, s = oracle_mod.quantize_rowwise_int8(w)
+    abits = a.view(np.uint16)
+    for i in range(abits.size):
+        exp = _nearest_fp16_exact(Fraction(float(a[i])) / 127)
+        assert s[i] == exp, (hex(abits[i]), hex(s[i]), hex(exp))
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "grid"])
+def test_int8_codes_brute_force_nearest_point(oracle_mod, kind):
+    g = synth.generator(17)
+    if kind == "normal":
+        w = synth.weight(32, 40, g).numpy()
+    elif kind == "t4":
+        w = synth.weight(32, 40, g, "t4").numpy()
+    else:
+        w = synth.exponent_rows(32, 40, g).numpy()
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    for r in range(w.shape[0]):
+        sv = Fraction(float(_f16(s[r])))
+        assert sv != 0
+        for c in range(w.shape[1]):
+            wv = Fraction(float(w[r, c]))
+            guess = int(round(float(wv / sv)))
+            assert q[r, c] == _nearest_code8(wv, sv, guess), (kind, r, c)
+
+
+def test_int8_ties_round_to_even(oracle_mod):
+    # absmax 127 -> s = 1; entries x.5 are exact ties
+    w = np.array([[127, 0.5, 1.5, 2.5, 3.5, 125.5, 126.5, -0.5, -1.5, -126.5]], dtype=np.float16)
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    assert s[0] == 0x3C00
+    assert q[0].tolist() == [127, 0, 2, 2, 4, 126, 126, 0, -2, -126]
+
+
+def test_int8_code_invariants_on_workload_shaped_data(oracle_mod):
+    g = synth.generator(19)
+    for dist in ("normal", "t4"):
+        w = synth.weight(256, 1024, g, dist).numpy()
+        q, s = oracle_mod.quantize_rowwise_int8(w)
+        wv = w.astype(np.float64)
+        sv = _f16(s).astype(np.float64)
+        assert q.dtype == np.int8 and q.min() >= -127 and q.max() <= 127
+        normal = sv >= 2.0 ** -14
+        err = np.abs(wv - sv[:, None] * q)
+        assert np.all(err[normal] <= sv[normal, None] / 2)
+        idx = np.abs(wv).argmax(axis=1)
+        assert np.all(np.abs(q[np.arange(len(q)), idx].astype(int)) == 127)
+        q2, s2 = oracle_mod.quantize_rowwise_int8(-w)
+        assert np.array_equal(s, s2) and np.array_equal(q2, -q)
+        # the INT8 scale is the INT4 one times 7/127 up to fp16 rounding
+        _, s4 = oracle_mod.quantize_codes(w)
+        s4v = _f16(s4).astype(np.float64)
+        assert np.all(np.abs(127 * sv - 7 * s4v) <= 127 * np.spacing(_f16(s)).astype(np.float64) / 2
+                      + 7 * np.spacing(_f16(s4)).astype(np.float64) / 2)
+
+
+def test_int8_zero_tiny_rows_and_subnormal_clamp(oracle_mod):
+    w = np.zeros((4, 8), dtype=np.float16)
+    w[1, 3] = _f16(63)       # 63 * 2^-24: a/127 < 2^-25 rounds to 0
+    w[2, 5] = -_f16(1)
+    w[3, :] = -0.0
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    assert np.all(s == 0) and np.all(q == 0)
+    w2 = np.zeros((1, 4), dtype=np.float16)
+    w2[0, 0] = _f16(190)     # 190/127 = 1.496 -> s = 2^-24; 190 -> clamp 127
+    w2[0, 1] = _f16(101)     # 101
+    w2[0, 2] = -_f16(150)    # -150 -> clamp -127
+    q2, s2 = oracle_mod.quantize_rowwise_int8(w2)
+    assert s2[0] == 1 and q2[0].tolist() == [127, 101, -127, 0]
+
+
+def test_int8_linear_vs_numpy_float64_matmul(oracle_mod):
+    g = synth.generator(23)
+    w = synth.weight(96, 512, g, "t4").numpy()
+    x = synth.activations(5, 512, g).numpy()
+    bias = synth.normal_fp16((96,), 0.5, g).numpy()
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    wh = q.astype(np.float64) * _f16(s).astype(np.float64)[:, None]
+    y, mag = oracle_mod.linear_int8(x, q, s, bias)
+    ref = x.astype(np.float64) @ wh.T + bias.astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
+    refmag = np.abs(x.astype(np.float64)) @ np.abs(wh).T + np.abs(bias.astype(np.float64))
+    assert np.allclose(mag, refmag, rtol=1e-12, atol=1e-13)
+    mi = np.array([0, 4, 2, 3]); ni = np.array([0, 95, 17, 50])
+    ys, ms = oracle_mod.linear_int8_at(x, q, s, mi, ni, bias)
+    assert np.array_equal(ys, y[mi, ni]) and np.array_equal(ms, mag[mi, ni])
+
+
+def test_int8_linear_one_hot_is_scaled_code(oracle_mod):
+    g = synth.generator(29)
+    w = synth.weight(40, 64, g, "t4").numpy()
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    x = synth.one_hot_activations(list(range(64)), 64).numpy()
+    y, _ = oracle_mod.linear_int8(x, q, s)
+    assert np.array_equal(y, (q.astype(np.float64) * _f16(s).astype(np.float64)[:, None]).T)
+
+
+def test_int8_geglu_vs_numpy_halves(oracle_mod):
+    from scipy.stats import norm
+    g = synth.generator(31)
+    f, k = 48, 256
+    w = synth.weight(2 * f, k, g, "t4").numpy()
+    x = synth.activations(3, k, g).numpy()
+    q, s = oracle_mod.quantize_rowwise_int8(w)
+    wh = q.astype(np.float64) * _f16(s).astype(np.float64)[:, None]
+    a = x.astype(np.float64) @ wh[:f].T
+    b = x.astype(np.float64) @ wh[f:].T
+    gg, aa, bb, ma, mb = oracle_mod.geglu_int8(x, q, s)
+    assert np.allclose(aa, a, rtol=1e-12, atol=1e-13)
+    assert np.allclose(bb, b, rtol=1e-12, atol=1e-13)
+    assert np.allclose(gg, a * norm.cdf(a) * b, rtol=1e-11, atol=1e-13)
+    mi = np.array([0, 2, 1]); ni = np.array([0, 47, 20])
+    gs = oracle_mod.geglu_int8_at(x, q, s, mi, ni)
+    assert np.array_equal(gs[0], gg[mi, ni])
