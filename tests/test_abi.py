@@ -1,5 +1,6 @@
-"""The C-ABI library loads, exports what include/w4a16.h declares, and
-rejects bad arguments before touching any device (runs without a GPU)."""
+"""The C-ABI library loads, exports what include/w4a16.h and include/w8a16.h
+declare, and rejects bad arguments before touching any device (runs without
+a GPU)."""
 import ctypes
 import os
 import re
@@ -9,16 +10,19 @@ import pytest
 from weight_only_int4_rowwise_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "w4a16.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w8a16.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libw4a16.so not built (python -m weight_only_int4_rowwise_amd.build)")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text))
+    names = set()
+    for header in HEADERS:
+        text = open(header).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text))
+    return names
 
 
 @pytest.fixture(scope="module")
@@ -69,7 +73,8 @@ def test_quantize_argument_checks(lib):
     assert q(None, 0, 32, None, None, None) == _lib.OK   # empty: pointers not looked at
 
 
-@pytest.mark.parametrize("fn", ["w4a16_linear", "w4a16_geglu_linear"])
+@pytest.mark.parametrize("fn", ["w4a16_linear", "w4a16_geglu_linear", "w8a16_linear",
+                                "w8a16_geglu_linear"])
 def test_linear_argument_checks(lib, fn):
     f = getattr(lib, fn)
     assert f(None, 1, 64, B, C, 16, None, D, None) == _lib.ERR_NULL
@@ -137,3 +142,53 @@ def test_buffer_size_limit(lib, fn, geglu):
     # size check (the call then fails on the fake pointers' alignment)
     n = 32768 if geglu else 65536
     assert f(A, 1, 12288, B, C, n, None, MIS, None) == _lib.ERR_ALIGN
+
+
+def test_int8_quantize_argument_checks(lib):
+    q = lib.quantize_rowwise_int8
+    assert q(None, 4, 32, B, C, None) == _lib.ERR_NULL
+    assert q(A, 4, 32, None, C, None) == _lib.ERR_NULL
+    assert q(A, -1, 32, B, C, None) == _lib.ERR_SHAPE
+    assert q(A, 4, 33, B, C, None) == _lib.ERR_SHAPE      # pairs of fp16 per load: k even
+    assert q(MIS, 4, 32, B, C, None) == _lib.ERR_ALIGN
+    assert q(A, 4, 32, MIS, C, None) == _lib.ERR_ALIGN
+    assert q(None, 0, 32, None, None, None) == _lib.OK
+
+
+def test_int8_prepacked_size_and_checks(lib):
+    assert lib.w8a16_prepacked_bytes(16, 128) == 2048
+    assert lib.w8a16_prepacked_bytes(17, 128) == 4096
+    assert lib.w8a16_prepacked_bytes(16, 160) == 4096
+    assert lib.w8a16_prepacked_bytes(36864, 12288) == 36864 * 12288
+    assert lib.w8a16_prepacked_bytes(16, 48) == -1
+    p = lib.w8a16_prepack
+    assert p(None, 16, 64, B, None) == _lib.ERR_NULL
+    assert p(A, 16, 48, B, None) == _lib.ERR_SHAPE
+    assert p(MIS, 16, 64, B, None) == _lib.ERR_ALIGN
+    assert p(None, 0, 64, None, None) == _lib.OK
+    g = lib.w8a16_geglu_linear_prepacked
+    assert g(A, 1, 64, B, C, 24, None, D, None) == _lib.ERR_SHAPE     # f % 16 != 0
+    assert lib.w8a16_linear_prepacked(A, 1, 48, B, C, 16, None, D, None) == _lib.ERR_SHAPE
+
+
+@pytest.mark.parametrize("fn,geglu", [("w8a16_linear", False), ("w8a16_geglu_linear", True),
+                                      ("w8a16_linear_prepacked", False),
+                                      ("w8a16_geglu_linear_prepacked", True)])
+def test_int8_buffer_size_limit(lib, fn, geglu):
+    """One byte per code: the INT8 weight reaches 2 GiB at half the rows of INT4."""
+    f = getattr(lib, fn)
+    k = 32768
+    rows = (1 << 31) // k                                 # codes == 2 GiB exactly
+    n = rows // 2 if geglu else rows
+    assert f(A, 1, k, B, C, n, None, D, None) == _lib.ERR_SHAPE
+    assert f(A, 1, k, B, C, n - 16, None, MIS, None) == _lib.ERR_ALIGN
+    # the GLM-130B FFN up-projection in INT8 (768 MiB) passes the size check
+    n = 32768 if geglu else 65536
+    assert f(A, 1, 12288, B, C, n, None, MIS, None) == _lib.ERR_ALIGN
+
+
+def test_int8_binding_refuses_cpu_tensors():
+    import torch
+    import weight_only_int4_rowwise_amd as w4
+    with pytest.raises(ValueError, match="no CPU path"):
+        w4.quantize_rowwise_int8(torch.zeros(4, 32, dtype=torch.float16))

@@ -14,6 +14,13 @@ the current HIP stream.  Every step of the computation runs in the library.
 
     qp = w4a16_prepack(q)                      # load-time tile layout, same bytes
     y = w4a16_linear_prepacked(x, qp, s)       # identical results, faster reads
+
+The INT8 variant (W8A16, include/w8a16.h; the pages' b-bit scale with
+b = 8: s = absmax / 127, one int8 code per weight) has the same calls:
+
+    c, s = quantize_rowwise_int8(w)            # c: cuda int8 [n][k]
+    y = w8a16_linear(x, c, s)
+    y = w8a16_linear_prepacked(x, w8a16_prepack(c), s)
 """
 from __future__ import annotations
 
@@ -28,6 +35,13 @@ __all__ = [
     "w4a16_prepack",
     "w4a16_linear_prepacked",
     "w4a16_geglu_linear_prepacked",
+    "quantize_rowwise_int8",
+    "w8a16_linear",
+    "w8a16_geglu_linear",
+    "w8a16_prepacked_bytes",
+    "w8a16_prepack",
+    "w8a16_linear_prepacked",
+    "w8a16_geglu_linear_prepacked",
     "W4A16Error",
     "library",
 ]
@@ -92,12 +106,14 @@ def _launch(fn, dev, *args):
 _PREPACKED_SIZES: dict = {}
 
 
-def _prepacked_size(lib, rows, k):
-    """w4a16_prepacked_bytes(rows, k), remembered per shape."""
-    key = (rows, k)
+def _prepacked_size(lib, rows, k, cb=4):
+    """w4a16_prepacked_bytes (cb = 4) or w8a16_prepacked_bytes (cb = 8) of
+    (rows, k), remembered per shape."""
+    key = (rows, k, cb)
     size = _PREPACKED_SIZES.get(key)
     if size is None:
-        size = int(lib.w4a16_prepacked_bytes(rows, k))
+        fn = lib.w4a16_prepacked_bytes if cb == 4 else lib.w8a16_prepacked_bytes
+        size = int(fn(rows, k))
         _PREPACKED_SIZES[key] = size
     return size
 
@@ -124,15 +140,15 @@ def quantize_rowwise_int4(w, q_out=None, s_out=None):
     return q_out, s_out
 
 
-def _linear_common(x, q, s, bias, out_cols, rows, y_out, name):
+def _linear_common(x, q, s, bias, out_cols, rows, y_out, name, cb=4):
     torch = _torch()
     _require(x, torch.float16, "x")
-    _require(q, torch.uint8, "q")
+    _require(q, torch.uint8 if cb == 4 else torch.int8, "q")
     _require(s, torch.float16, "s")
     if x.dim() != 2 or q.dim() != 2 or s.dim() != 1:
-        raise ValueError(f"{name}: x [m][k], q [rows][k/2], s [rows] expected")
+        raise ValueError(f"{name}: x [m][k], q [rows][{'k/2' if cb == 4 else 'k'}], s [rows] expected")
     m, k = x.shape
-    if q.shape[0] != rows or q.shape[1] * 2 != k or s.shape[0] != rows:
+    if q.shape[0] != rows or q.shape[1] * 8 // cb != k or s.shape[0] != rows:
         raise ValueError(f"{name}: shape mismatch x {tuple(x.shape)} q {tuple(q.shape)} s {tuple(s.shape)}")
     dev = x.get_device()
     _same_device(q, dev, "q", name)
@@ -204,7 +220,7 @@ def w4a16_prepack(q, q_out=None):
     return q_out
 
 
-def _prepacked_common(x, qp, s, bias, out_cols, rows, y_out, name):
+def _prepacked_common(x, qp, s, bias, out_cols, rows, y_out, name, cb=4):
     torch = _torch()
     lib = _lib.load()
     _require(x, torch.float16, "x")
@@ -213,7 +229,7 @@ def _prepacked_common(x, qp, s, bias, out_cols, rows, y_out, name):
     if x.dim() != 2 or s.dim() != 1 or s.shape[0] != rows:
         raise ValueError(f"{name}: x [m][k] and s [{rows}] expected")
     m, k = x.shape
-    size = _prepacked_size(lib, rows, k)
+    size = _prepacked_size(lib, rows, k, cb)
     if size < 0 or qp.numel() != size:
         raise ValueError(f"{name}: prepacked weight must hold {size} bytes for {rows} x {k}")
     dev = x.get_device()
@@ -256,4 +272,113 @@ def w4a16_geglu_linear_prepacked(x, qp, s, bias=None, y_out=None):
                  x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
                  None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_geglu_linear_prepacked")
+    return y_out
+
+
+# --------------------------------------------------------------------------
+# INT8 variant (include/w8a16.h)
+# --------------------------------------------------------------------------
+
+def quantize_rowwise_int8(w, q_out=None, s_out=None):
+    """W fp16 [n][k] (k even) -> (codes int8 [n][k], scales fp16 [n]); s = fp16(absmax / 127)."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(w, torch.float16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [out_features][in_features]")
+    n, k = w.shape
+    if q_out is None:
+        q_out = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    if s_out is None:
+        s_out = torch.empty((n,), dtype=torch.float16, device=w.device)
+    _require(q_out, torch.int8, "q_out")
+    _require(s_out, torch.float16, "s_out")
+    if tuple(q_out.shape) != (n, k) or tuple(s_out.shape) != (n,):
+        raise ValueError("output shape mismatch")
+    dev = w.get_device()
+    _same_device(q_out, dev, "q_out", "quantize_rowwise_int8")
+    _same_device(s_out, dev, "s_out", "quantize_rowwise_int8")
+    st = _launch(lib.quantize_rowwise_int8, dev, w.data_ptr(), n, k, q_out.data_ptr(),
+                 s_out.data_ptr())
+    _lib.check(st, "quantize_rowwise_int8")
+    return q_out, s_out
+
+
+def w8a16_linear(x, q, s, bias=None, y_out=None):
+    """y[m][n] = fp16(s * (x . q^T) + bias) over INT8 codes q [n][k]."""
+    lib = _lib.load()
+    n = q.shape[0]
+    m, k, y_out = _linear_common(x, q, s, bias, n, n, y_out, "w8a16_linear", cb=8)
+    st = _launch(lib.w8a16_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w8a16_linear")
+    return y_out
+
+
+def w8a16_geglu_linear(x, q, s, bias=None, y_out=None):
+    """GeGLU over INT8 codes q [2f][k]: y[m][f] = fp16(GELU(a) * b)."""
+    lib = _lib.load()
+    rows = q.shape[0]
+    if rows % 2:
+        raise ValueError("w8a16_geglu_linear: q must have an even number of rows (2f)")
+    f = rows // 2
+    m, k, y_out = _linear_common(x, q, s, bias, f, rows, y_out, "w8a16_geglu_linear", cb=8)
+    st = _launch(lib.w8a16_geglu_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w8a16_geglu_linear")
+    return y_out
+
+
+def w8a16_prepacked_bytes(n: int, k: int) -> int:
+    """Bytes of the prepacked layout of INT8 codes [n][k] (-1 for bad sizes)."""
+    return int(_lib.load().w8a16_prepacked_bytes(int(n), int(k)))
+
+
+def w8a16_prepack(q, q_out=None):
+    """INT8 codes [n][k] -> prepacked tile layout (uint8, 1-D)."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(q, torch.int8, "q")
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D [n][k]")
+    n, k = q.shape
+    size = lib.w8a16_prepacked_bytes(n, k)
+    if size < 0:
+        raise ValueError(f"w8a16_prepack: bad shape n={n} k={k} (k % 32 must be 0)")
+    if q_out is None:
+        q_out = torch.empty((size,), dtype=torch.uint8, device=q.device)
+    _require(q_out, torch.uint8, "q_out")
+    if q_out.numel() != size:
+        raise ValueError(f"w8a16_prepack: q_out must hold {size} bytes")
+    _same_device(q_out, q.get_device(), "q_out", "w8a16_prepack")
+    st = _launch(lib.w8a16_prepack, q.get_device(), q.data_ptr(), n, k, q_out.data_ptr())
+    _lib.check(st, "w8a16_prepack")
+    return q_out
+
+
+def w8a16_linear_prepacked(x, qp, s, bias=None, y_out=None):
+    """w8a16_linear with the codes in the prepacked layout (n = len(s))."""
+    n = s.shape[0]
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, n, n, y_out, "w8a16_linear_prepacked", cb=8)
+    st = _launch(lib.w8a16_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w8a16_linear_prepacked")
+    return y_out
+
+
+def w8a16_geglu_linear_prepacked(x, qp, s, bias=None, y_out=None):
+    """w8a16_geglu_linear with the codes in the prepacked layout (f = len(s) / 2)."""
+    rows = s.shape[0]
+    if rows % 2:
+        raise ValueError("w8a16_geglu_linear_prepacked: s must have 2f entries")
+    f = rows // 2
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, f, rows, y_out,
+                                         "w8a16_geglu_linear_prepacked", cb=8)
+    st = _launch(lib.w8a16_geglu_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w8a16_geglu_linear_prepacked")
     return y_out

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 # Status codes of include/w4a16.h
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_DEVICE = range(6)
 
-# Every symbol include/w4a16.h declares.
+# Every symbol include/w4a16.h and include/w8a16.h declare.
 EXPORTS = (
     "quantize_rowwise_int4",
     "w4a16_linear",
@@ -26,6 +26,13 @@ EXPORTS = (
     "w4a16_status_string",
     "w4a16_last_error",
     "w4a16_abi_version",
+    "quantize_rowwise_int8",
+    "w8a16_linear",
+    "w8a16_geglu_linear",
+    "w8a16_prepacked_bytes",
+    "w8a16_prepack",
+    "w8a16_linear_prepacked",
+    "w8a16_geglu_linear_prepacked",
 )
 
 ABI_VERSION = 1
@@ -68,6 +75,16 @@ def load() -> ctypes.CDLL:
     lib.w4a16_linear_prepacked.restype = ctypes.c_int
     lib.w4a16_geglu_linear_prepacked.argtypes = [P, I, I, P, P, I, P, P, P]
     lib.w4a16_geglu_linear_prepacked.restype = ctypes.c_int
+    lib.quantize_rowwise_int8.argtypes = [P, I, I, P, P, P]
+    lib.quantize_rowwise_int8.restype = ctypes.c_int
+    for fn in ("w8a16_linear", "w8a16_geglu_linear", "w8a16_linear_prepacked",
+               "w8a16_geglu_linear_prepacked"):
+        getattr(lib, fn).argtypes = [P, I, I, P, P, I, P, P, P]
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.w8a16_prepacked_bytes.argtypes = [I, I]
+    lib.w8a16_prepacked_bytes.restype = ctypes.c_int64
+    lib.w8a16_prepack.argtypes = [P, I, I, P, P]
+    lib.w8a16_prepack.restype = ctypes.c_int
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_last_error.argtypes = []

@@ -1,6 +1,8 @@
-// C ABI of the W4A16 library: argument checks, kernel selection, error
-// mapping.  Contract and citations: include/w4a16.h.
+// C ABI of the W4A16 library and its W8A16 variant: argument checks,
+// kernel selection, error mapping.  Contract and citations: include/w4a16.h
+// and include/w8a16.h.
 #include "../../include/w4a16.h"
+#include "../../include/w8a16.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -9,14 +11,18 @@
 namespace w4a16 {
 hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
                            hipStream_t stream);
+hipError_t launch_quantize_int8(const void *w, int64_t n, int64_t k, void *codes, void *scales,
+                                hipStream_t stream);
 hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
+                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
                          hipStream_t stream);
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          bool tiled, hipStream_t stream);
+                          bool tiled, int cb, hipStream_t stream);
 int64_t prepacked_bytes(int64_t n, int64_t k);
 hipError_t launch_prepack(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
+int64_t prepacked_bytes_int8(int64_t n, int64_t k);
+hipError_t launch_prepack_int8(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
 }  // namespace w4a16
 
 namespace {
@@ -50,14 +56,15 @@ w4a16_status from_hip(hipError_t e)
 
 // Sizes first: an empty call (m == 0 or rows == 0) is valid whatever the
 // pointers are (torch hands out NULL for empty tensors).
-w4a16_status check_gemm_shape(int64_t m, int64_t k, int64_t rows, bool tiled)
+w4a16_status check_gemm_shape(int64_t m, int64_t k, int64_t rows, bool tiled, int cb)
 {
     if (m < 0 || rows < 0 || k <= 0 || k % 32 != 0 || m > kMaxDim || rows > kMaxDim ||
         k > kMaxDim || m * k > (int64_t(1) << 40) || m * rows > (int64_t(1) << 40))
         return W4A16_ERR_SHAPE;
     // the kernels address the activations and the weight with 32-bit
     // buffer offsets
-    const int64_t wbytes = tiled ? w4a16::prepacked_bytes(rows, k) : rows * (k / 2);
+    const int64_t wbytes = cb == 8 ? (tiled ? w4a16::prepacked_bytes_int8(rows, k) : rows * k)
+                                   : (tiled ? w4a16::prepacked_bytes(rows, k) : rows * (k / 2));
     if (2 * m * k >= kMaxBufferBytes || wbytes >= kMaxBufferBytes)
         return W4A16_ERR_SHAPE;
     return W4A16_OK;
@@ -75,11 +82,11 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
 }
 
 w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, const void *s,
-                        int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
+                        int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
                         void *stream)
 {
     const int64_t rows = geglu ? 2 * n_out : n_out;
-    w4a16_status st = check_gemm_shape(m, k, rows, tiled);
+    w4a16_status st = check_gemm_shape(m, k, rows, tiled, cb);
     if (st != W4A16_OK)
         return st;
     if (m == 0 || n_out == 0)
@@ -90,7 +97,7 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (m <= kDecodeMaxM) {
-        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, hs);
+        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
     } else if (m <= 2 * kDecodeMaxM) {
         // 64 < m <= 128: the first 64 tokens, then the rest, each through
         // the decode kernel.  The weights stream twice, but every CU stays
@@ -99,14 +106,14 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
         // attention-out 12288 x 12288 at m = 96: 59 against 83 us).
         // Outputs depend only on their own token row, so the split changes
         // no result bits.
-        e = w4a16::launch_decode(x, (int)kDecodeMaxM, k, q, s, n_out, bias, y, geglu, tiled, hs);
+        e = w4a16::launch_decode(x, (int)kDecodeMaxM, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
         if (e == hipSuccess)
             e = w4a16::launch_decode(static_cast<const uint16_t *>(x) + kDecodeMaxM * k,
                                      (int)(m - kDecodeMaxM), k, q, s, n_out, bias,
                                      static_cast<uint16_t *>(y) + kDecodeMaxM * n_out, geglu,
-                                     tiled, hs);
+                                     tiled, cb, hs);
     } else {
-        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, hs);
+        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
     }
     return from_hip(e);
 }
@@ -134,7 +141,7 @@ w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k, const void *
                           const void *scales_fp16, int64_t n, const void *bias_fp16, void *y_fp16,
                           void *stream)
 {
-    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, false,
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, false, 4,
                       stream);
 }
 
@@ -144,7 +151,7 @@ w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const 
 {
     if (f > kMaxDim / 2)
         return W4A16_ERR_SHAPE;
-    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, false,
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, false, 4,
                       stream);
 }
 
@@ -174,7 +181,7 @@ w4a16_status w4a16_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
                                     const void *q_prepacked, const void *scales_fp16, int64_t n,
                                     const void *bias_fp16, void *y_fp16, void *stream)
 {
-    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, n, bias_fp16, y_fp16, false, true,
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, n, bias_fp16, y_fp16, false, true, 4,
                       stream);
 }
 
@@ -186,8 +193,83 @@ w4a16_status w4a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t
     // the gate / value boundary must fall on a 16-row tile boundary
     if (f > kMaxDim / 2 || f % 16 != 0)
         return W4A16_ERR_SHAPE;
-    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true,
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true, 4,
                       stream);
+}
+
+w4a16_status quantize_rowwise_int8(const void *w_fp16, int64_t n, int64_t k, void *codes_i8,
+                                   void *scales_fp16, void *stream)
+{
+    if (n < 0 || k < 2 || k % 2 != 0 || n > 0x7FFFFFFF || k > kMaxDim)
+        return W4A16_ERR_SHAPE;
+    if (n == 0)
+        return W4A16_OK;
+    if (!w_fp16 || !codes_i8 || !scales_fp16)
+        return W4A16_ERR_NULL;
+    if (!aligned16(w_fp16) || !aligned16(codes_i8) || !aligned16(scales_fp16))
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_quantize_int8(w_fp16, n, k, codes_i8, scales_fp16,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status w8a16_linear(const void *x_fp16, int64_t m, int64_t k, const void *codes_i8,
+                          const void *scales_fp16, int64_t n, const void *bias_fp16, void *y_fp16,
+                          void *stream)
+{
+    return run_linear(x_fp16, m, k, codes_i8, scales_fp16, n, bias_fp16, y_fp16, false, false, 8,
+                      stream);
+}
+
+w4a16_status w8a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const void *codes_i8,
+                                const void *scales_fp16, int64_t f, const void *bias_fp16,
+                                void *y_fp16, void *stream)
+{
+    if (f > kMaxDim / 2)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, codes_i8, scales_fp16, f, bias_fp16, y_fp16, true, false, 8,
+                      stream);
+}
+
+int64_t w8a16_prepacked_bytes(int64_t n, int64_t k)
+{
+    if (n < 0 || k <= 0 || k % 32 != 0 || n > kMaxDim || k > kMaxDim)
+        return -1;
+    return w4a16::prepacked_bytes_int8(n, k);
+}
+
+w4a16_status w8a16_prepack(const void *codes_i8, int64_t n, int64_t k, void *codes_prepacked,
+                           void *stream)
+{
+    if (w8a16_prepacked_bytes(n, k) < 0)
+        return W4A16_ERR_SHAPE;
+    if (n == 0)
+        return W4A16_OK;
+    if (!codes_i8 || !codes_prepacked)
+        return W4A16_ERR_NULL;
+    if (!aligned16(codes_i8) || !aligned16(codes_prepacked))
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_prepack_int8(codes_i8, n, k, codes_prepacked,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status w8a16_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                    const void *codes_prepacked, const void *scales_fp16, int64_t n,
+                                    const void *bias_fp16, void *y_fp16, void *stream)
+{
+    return run_linear(x_fp16, m, k, codes_prepacked, scales_fp16, n, bias_fp16, y_fp16, false, true,
+                      8, stream);
+}
+
+w4a16_status w8a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                          const void *codes_prepacked, const void *scales_fp16,
+                                          int64_t f, const void *bias_fp16, void *y_fp16,
+                                          void *stream)
+{
+    // the gate / value boundary must fall on a 16-row tile boundary
+    if (f > kMaxDim / 2 || f % 16 != 0)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, codes_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true,
+                      8, stream);
 }
 
 const char *w4a16_status_string(int status)

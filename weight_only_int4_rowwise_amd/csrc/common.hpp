@@ -1,4 +1,5 @@
-// Device helpers shared by the gfx950 kernels of the W4A16 library.
+// Device helpers shared by the gfx950 kernels of the W4A16 library (and of
+// its INT8 variant, W8A16: one two's-complement code per byte, [n][k]).
 //
 // Packed weight layout (include/w4a16.h): uint8 [n][k/2], code 2j in the low
 // nibble of byte j, code 2j+1 in the high nibble, 4-bit two's complement,
@@ -88,6 +89,38 @@ template <bool PREPACKED>
 __device__ __forceinline__ half8 dequant8_of(uint32_t packed)
 {
     return PREPACKED ? dequant8(packed) : dequant8_rm(packed);
+}
+
+// ---------------------------------------------------------------------------
+// INT8 -> FP16 dequantization of two dwords (8 codes in their natural
+// order) into one MFMA operand.  A code q in [-127, 127] as the offset
+// byte u = q + 128 (q's two's-complement byte with its top bit flipped)
+// under the exponent byte 0x64 is the binary16 1024 + u, exact; one packed
+// f16 subtract of 1152 returns q.  One v_perm_b32 builds two such halves
+// from two code bytes and a constant 0x64 byte (selector bytes 0..3 pick
+// the code dword, 4 picks the constant).  The prepacked layout stores the
+// offset bytes (8 VALU ops per 8 codes); the row-major one stores two's
+// complement and adds one xor per dword (10 ops).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ half8 dequant8_i8(uint32_t lo, uint32_t hi)
+{
+    const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, bits_to_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - bias);
+    r[1] = __builtin_bit_cast(uint32_t, bits_to_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - bias);
+    r[2] = __builtin_bit_cast(uint32_t, bits_to_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - bias);
+    r[3] = __builtin_bit_cast(uint32_t, bits_to_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - bias);
+    return __builtin_bit_cast(half8, r);
+}
+
+template <bool PREPACKED>
+__device__ __forceinline__ half8 dequant8_i8_of(uint32_t lo, uint32_t hi)
+{
+    if (!PREPACKED) {
+        lo ^= 0x80808080u;
+        hi ^= 0x80808080u;
+    }
+    return dequant8_i8(lo, hi);
 }
 
 // Row-major packed dword -> the prepacked nibble order read by dequant8.
@@ -207,6 +240,14 @@ __device__ __forceinline__ uint32_t piece_step_off(uint32_t kc)
 __host__ __device__ __forceinline__ int64_t weight_bytes(bool tiled, int64_t rows, int64_t k)
 {
     return tiled ? ((rows + 15) / 16) * ((k + 127) / 128) * 1024 : rows * (k / 2);
+}
+
+// The same for cb-bit codes (4: two per byte, 1 KB tiles; 8: one per byte,
+// 2 KB tiles of 16 rows x 128 indices).
+__host__ __device__ __forceinline__ int64_t code_weight_bytes(int cb, bool tiled, int64_t rows, int64_t k)
+{
+    return cb == 8 ? (tiled ? ((rows + 15) / 16) * ((k + 127) / 128) * 2048 : rows * k)
+                   : weight_bytes(tiled, rows, k);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p)

@@ -22,6 +22,9 @@
 //  * The row scale is constant along the sum, so it is applied once to the
 //    fp32 sum in the epilogue instead of to every weight; then the bias,
 //    the optional GeGLU, and one fp16 rounding.
+//  * CB = 8 instantiates the INT8 variant (W8A16: the pages' b-bit scale
+//    with b = 8, one code per byte): two 16-byte weight loads per lane,
+//    row group and 128 indices, dequant8_i8; everything else is shared.
 #include "common.hpp"
 
 namespace w4a16 {
@@ -96,7 +99,8 @@ struct TokenTile {
     static_assert(MB == 1 ? (MR == 4 || MR == 8 || MR == 16) : MR == 16 * MB, "token rows");
 };
 
-template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED,
+          int CB>
 __global__ __launch_bounds__(W * kWave) void decode_kernel(
     const uint16_t *__restrict__ x, int m, int64_t k, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, int64_t n_out, const uint16_t *__restrict__ bias,
@@ -105,7 +109,10 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     (void)TokenTile<MB, MR>{};
     static_assert(!GEGLU || NGW % 2 == 0, "GeGLU pairs gate and value row groups");
     static_assert(W % RG == 0, "row sets split the wavefronts evenly");
+    static_assert(CB == 4 || CB == 8, "INT4 or INT8 codes");
     constexpr int KS = W / RG;
+    constexpr int WP = CB / 4;                // 16-byte weight pieces per lane, row group and 128 indices
+    static_assert(NGW * KU * WP * (D - 1) <= 63, "outstanding weight loads fit the vmcnt counter");
     constexpr int KC = 128 * KU;              // reduction indices per chunk
     constexpr int RP = KC / 8;                // 16-byte pieces per activation row per chunk
     // 16 or more token rows: activations by LDS DMA into XOR-swizzled rows.
@@ -135,11 +142,11 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     const int r16 = lane % 16;
     const int g = lane / 16;
     const int64_t o0 = ((int64_t)blockIdx.x * RG + rgi) * OUTW;   // first output of this wave
-    const int64_t kb = k / 2;
+    const int64_t kb = k * CB / 8;             // bytes of a row-major row
     const int64_t kt = ceil_div(k, 128);
 
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, code_weight_bytes(CB, TILED, rows, k));
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (int64_t)m * k * 2);
 
     // Per-lane constant part of each weight load offset.  Rows past the
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         if (!TILED && o >= n_out)
             o = n_out - 1;
         const int64_t row = (GEGLU && j >= NGW / 2) ? n_out + o : o;
-        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 + 16 * lane)
-                         : (uint32_t)(row * kb + 16 * g);
+        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 * WP + 16 * lane)
+                         : (uint32_t)(row * kb + 16 * WP * g);
     }
     const uint32_t k32 = (uint32_t)k;
 
@@ -171,15 +178,17 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     const int64_t rounds = ceil_div(nch, KS);
 
     // Chunk c of this wave, piece p: reduction indices c KC + 128 p + 32 g.
-    // The wave-uniform step (c KC + 128 p) / 2 bytes (row-major) or tile
-    // c KU + p (prepacked) is added to the per-lane base.
-    auto load_w = [&](int64_t r, u32x4(&wd)[NGW][KU]) {
+    // The wave-uniform step (c KC + 128 p) CB / 8 bytes (row-major) or tile
+    // c KU + p (prepacked) is added to the per-lane base.  INT8 codes take
+    // two 16-byte loads per piece: the lane's next 16 bytes (row-major) or
+    // the tile's second KB (prepacked).
+    auto load_w = [&](int64_t r, u32x4(&wd)[NGW][KU * WP]) {
         const uint32_t c = (uint32_t)(r * KS + kp);
         const bool live = c < (uint32_t)nch;
 #pragma unroll
         for (int p = 0; p < KU; ++p) {
             const uint32_t u = c * KC + 128 * p;
-            uint32_t step = TILED ? (c * KU + p) * 1024u : u / 2;
+            uint32_t step = TILED ? (c * KU + p) * 1024u * WP : u * CB / 8;
             if (!live)
                 step = kOutOfRange;
 #pragma unroll
@@ -187,7 +196,9 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
                 uint32_t off = wbase[j] + step;
                 if (!EVEN && !TILED && u + 32 * g >= k32)
                     off = kOutOfRange;                 // ragged last piece, row-major only
-                wd[j][p] = buf_load16_stream(wrs, off);
+#pragma unroll
+                for (int h = 0; h < WP; ++h)
+                    wd[j][WP * p + h] = buf_load16_stream(wrs, off + h * (TILED ? 1024u : 16u));
             }
         }
     };
@@ -257,7 +268,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     // overwrites (the fences order only LDS accesses around it).
     auto publish = [&]() {
         if constexpr (XDMA) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU * WP));
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         rdoff[t] = 16 * (XDMA ? ((4 * g + t) ^ brow) : 4 * g + t);
-    auto compute = [&](int buf, const u32x4(&wd)[NGW][KU]) {
+    auto compute = [&](int buf, const u32x4(&wd)[NGW][KU * WP]) {
 #pragma unroll
         for (int p = 0; p < KU; ++p)
 #pragma unroll
@@ -283,7 +294,12 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
                         xrd + buf * STAGE + (16 * b * LD + 128 * p) * 2 + rdoff[t]));
 #pragma unroll
                 for (int j = 0; j < NGW; ++j) {
-                    const half8 a = dequant8_of<TILED>(wd[j][p][t]);
+                    half8 a;
+                    if constexpr (CB == 4)
+                        a = dequant8_of<TILED>(wd[j][p][t]);
+                    else
+                        a = dequant8_i8_of<TILED>(wd[j][2 * p + t / 2][2 * (t % 2)],
+                                                  wd[j][2 * p + t / 2][2 * (t % 2) + 1]);
 #pragma unroll
                     for (int b = 0; b < MB; ++b)
                         acc[j][b][t % CH] = mfma16x16x32(a, bx[b], acc[j][b][t % CH]);
@@ -297,14 +313,14 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     // copies, which would force the loads to retire early).  Scheduling barriers keep each round's loads at its
     // top, activations first: left alone, the compiler sinks them towards
     // their first use and the prefetch distance collapses.
-    u32x4 wr[D][NGW][KU];
+    u32x4 wr[D][NGW][KU * WP];
     load_x(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D - 1; ++i)
         load_w(i, wr[i]);
     if constexpr (XDMA)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU * (D - 1)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NGW * KU * WP * (D - 1)));
     store_x(0);
     publish();
     constexpr int U = D % 2 == 0 ? D : 2 * D;
@@ -447,28 +463,29 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     }
 }
 
-template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED>
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool EVEN, bool GEGLU, bool TILED,
+          int CB>
 void launch_decode_t(const void *x, int m, int64_t k, const void *packed, const void *scales,
                      int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
     constexpr int OUTW = GEGLU ? 8 * NGW : 16 * NGW;
     const unsigned grid = (unsigned)ceil_div(n_out, OUTW * RG);
-    hipLaunchKernelGGL((decode_kernel<KU, RG, W, D, MB, MR, NGW, EVEN, GEGLU, TILED>),
+    hipLaunchKernelGGL((decode_kernel<KU, RG, W, D, MB, MR, NGW, EVEN, GEGLU, TILED, CB>),
                        dim3(grid), dim3(W * kWave), 0, stream, static_cast<const uint16_t *>(x), m, k,
                        static_cast<const uint8_t *>(packed), static_cast<const uint16_t *>(scales),
                        n_out, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
 }
 
 // Reduction evenness of a launch.
-template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool GEGLU, bool TILED>
+template <int KU, int RG, int W, int D, int MB, int MR, int NGW, bool GEGLU, bool TILED, int CB>
 void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const void *scales,
                      int64_t n_out, const void *bias, void *y, hipStream_t stream)
 {
     if (k % (128 * KU * (W / RG)) == 0)
-        launch_decode_t<KU, RG, W, D, MB, MR, NGW, true, GEGLU, TILED>(x, m, k, packed, scales,
+        launch_decode_t<KU, RG, W, D, MB, MR, NGW, true, GEGLU, TILED, CB>(x, m, k, packed, scales,
                                                                        n_out, bias, y, stream);
     else
-        launch_decode_t<KU, RG, W, D, MB, MR, NGW, false, GEGLU, TILED>(x, m, k, packed, scales,
+        launch_decode_t<KU, RG, W, D, MB, MR, NGW, false, GEGLU, TILED, CB>(x, m, k, packed, scales,
                                                                         n_out, bias, y, stream);
 }
 
@@ -489,15 +506,16 @@ void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const 
 // (each activation operand feeds more MFMAs).  At m > 48 tall weights keep
 // three weight register sets in flight (D = 3): the round there is long
 // enough that two sets leave the wave waiting on the loads.
-template <bool GEGLU, bool TILED>
+template <bool GEGLU, bool TILED, int CB>
 static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const void *packed,
                                        const void *scales, int64_t n_out, const void *bias, void *y,
                                        hipStream_t stream)
 {
+    static_assert(CB == 4, "INT4 launch shapes");
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
-#define W4_DEC(KU, RG, W, D, MB, MR, NGW)                                                         \
-    launch_decode_e<KU, RG, W, D, MB, MR, NGW, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, \
-                                                             y, stream)
+#define W4_DEC(KU, RG, W, D, MB, MR, NGW)                                                     \
+    launch_decode_e<KU, RG, W, D, MB, MR, NGW, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, \
+                                                                 bias, y, stream)
     if constexpr (GEGLU) {
         // a wavefront always holds gate and value groups: NGW even.
         // Height bands: 3 from 49152 rows, 2 from 24576, 1 from 12288, 0 below.
@@ -569,15 +587,104 @@ static hipError_t launch_decode_layout(const void *x, int m, int64_t k, const vo
     return hipGetLastError();
 }
 
+// INT8 launch shapes: the INT4 bands with the chunk halved (128 indices of
+// one-byte codes are the bytes of 256 INT4 indices, so a wave's loads per
+// round stay the same size) and two weight register sets in flight; the
+// tallest GeGLU weights at 16 < m <= 32 take two row groups per wave.  The
+// INT4 shapes would need up to twice the weight registers and spill.
+template <bool GEGLU, bool TILED>
+static hipError_t launch_decode_layout8(const void *x, int m, int64_t k, const void *packed,
+                                        const void *scales, int64_t n_out, const void *bias,
+                                        void *y, hipStream_t stream)
+{
+    constexpr int CB = 8;
+    const int64_t rows = GEGLU ? 2 * n_out : n_out;
+#define W4_DEC(KU, RG, W, D, MB, MR, NGW)                                                     \
+    launch_decode_e<KU, RG, W, D, MB, MR, NGW, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, \
+                                                                 bias, y, stream)
+    if constexpr (GEGLU) {
+        const int b = rows >= 49152 ? 3 : rows >= 24576 ? 2 : rows >= 12288 ? 1 : 0;
+        if (m <= 4)
+            b == 3   ? W4_DEC(1, 4, 8, 2, 1, 4, 2)
+            : b == 2 ? W4_DEC(1, 2, 4, 2, 1, 4, 2)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 1, 4, 2)
+                     : W4_DEC(1, 1, 8, 2, 1, 4, 2);
+        else if (m <= 8)
+            b == 3 ? W4_DEC(1, 4, 4, 2, 1, 8, 2)
+            : b    ? W4_DEC(1, 2, 8, 2, 1, 8, 2)
+                   : W4_DEC(1, 1, 8, 2, 1, 8, 2);
+        else if (m <= 16)
+            b == 3 ? W4_DEC(1, 8, 16, 2, 1, 16, 2)
+            : b    ? W4_DEC(1, 2, 8, 2, 1, 16, 2)
+                   : W4_DEC(1, 1, 8, 2, 1, 16, 2);
+        else if (m <= 32)
+            b == 3   ? W4_DEC(1, 4, 16, 2, 2, 32, 2)
+            : b == 2 ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
+            : b == 1 ? W4_DEC(1, 2, 8, 2, 2, 32, 2)
+                     : W4_DEC(1, 1, 4, 2, 2, 32, 2);
+        else if (m <= 48)
+            b == 3   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
+            : b == 2 ? W4_DEC(1, 2, 4, 2, 3, 48, 4)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 4)
+                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
+        else
+            b == 3 ? W4_DEC(1, 8, 16, 2, 4, 64, 2)
+            : b    ? W4_DEC(1, 2, 4, 2, 4, 64, 2)
+                   : W4_DEC(1, 1, 4, 2, 4, 64, 2);
+    } else {
+        const int b = rows >= 49152 ? 4 : rows >= 24576 ? 3 : rows >= 16384 ? 2 : rows >= 8192 ? 1 : 0;
+        if (m <= 4)
+            b == 4   ? W4_DEC(1, 4, 4, 2, 1, 4, 1)
+            : b == 3 ? W4_DEC(1, 3, 6, 2, 1, 4, 1)
+            : b      ? W4_DEC(1, 1, 4, 2, 1, 4, 1)
+                     : W4_DEC(1, 1, 8, 2, 1, 4, 1);
+        else if (m <= 8)
+            b == 4   ? W4_DEC(1, 4, 4, 2, 1, 8, 1)
+            : b >= 2 ? W4_DEC(1, 1, 4, 2, 1, 8, 3)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 1, 4, 2, 1, 8, 1) : W4_DEC(2, 3, 12, 2, 1, 8, 1))
+                     : W4_DEC(1, 2, 8, 2, 1, 8, 1);
+        else if (m <= 16)
+            b == 4                           ? W4_DEC(1, 4, 4, 2, 1, 16, 2)
+            : b == 3                         ? W4_DEC(1, 3, 12, 2, 1, 16, 3)
+            : b == 2 || (b == 1 && k < 4096) ? W4_DEC(1, 1, 4, 2, 1, 16, 3)
+            : b == 1                         ? W4_DEC(1, 1, 8, 2, 1, 16, 3)
+                                             : W4_DEC(1, 2, 8, 2, 1, 16, 1);
+        else if (m <= 32)
+            b == 4   ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
+            : b >= 2 ? W4_DEC(1, 3, 12, 2, 2, 32, 3)
+            : b == 1 ? (k <= 4096 ? W4_DEC(1, 2, 8, 2, 2, 32, 2) : W4_DEC(1, 1, 4, 2, 2, 32, 3))
+                     : W4_DEC(1, 1, 4, 2, 2, 32, 2);
+        else if (m <= 48)
+            b == 4   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
+            : b >= 2 ? W4_DEC(1, 3, 12, 2, 3, 48, 3)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 3)
+                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
+        else
+            b == 4   ? W4_DEC(1, 8, 16, 2, 4, 64, 2)
+            : b >= 2 ? W4_DEC(1, 3, 12, 2, 4, 64, 3)
+            : b == 1 ? W4_DEC(1, 1, 4, 2, 4, 64, 3)
+                     : W4_DEC(1, 1, 4, 2, 4, 64, 2);
+    }
+#undef W4_DEC
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled,
+                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
                          hipStream_t stream)
 {
+#define W4_LAYOUT(G, T, C) launch_decode_layout<G, T, C>(x, m, k, packed, scales, n_out, bias, y, stream)
+#define W8_LAYOUT(G, T) launch_decode_layout8<G, T>(x, m, k, packed, scales, n_out, bias, y, stream)
+    if (cb == 8) {
+        if (geglu)
+            return tiled ? W8_LAYOUT(true, true) : W8_LAYOUT(true, false);
+        return tiled ? W8_LAYOUT(false, true) : W8_LAYOUT(false, false);
+    }
     if (geglu)
-        return tiled ? launch_decode_layout<true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                     : launch_decode_layout<true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
-    return tiled ? launch_decode_layout<false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                 : launch_decode_layout<false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return tiled ? W4_LAYOUT(true, true, 4) : W4_LAYOUT(true, false, 4);
+    return tiled ? W4_LAYOUT(false, true, 4) : W4_LAYOUT(false, false, 4);
+#undef W8_LAYOUT
+#undef W4_LAYOUT
 }
 
 }  // namespace w4a16

@@ -30,6 +30,9 @@
 //    steps past the end read zeros.  The step loop is unrolled twice over
 //    two weight register sets, so no register copy forces a load to retire
 //    early.
+//  * INT8 codes (the W8A16 variant, one byte per code) take two 16-byte
+//    weight loads per lane and row group per step and dequantize with
+//    dequant8_i8; everything else is shared.
 #include "common.hpp"
 
 namespace w4a16 {
@@ -38,7 +41,7 @@ constexpr int kPBK = 128;                 // reduction step
 constexpr int kPRowBytes = 2 * kPBK;      // bytes of one token row per step
 constexpr int kPThreads = 256;
 
-template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED>
+template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED, int CB>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *__restrict__ x,
                                                             int64_t m, int64_t k,
                                                             const uint8_t *__restrict__ packed,
@@ -49,6 +52,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
                                                             int tiles_m)
 {
     static_assert(!GEGLU || WN % 2 == 0, "GeGLU pairs gate and value row groups");
+    static_assert(CB == 4 || CB == 8, "INT4 or INT8 codes");
+    constexpr int WP = CB / 4;                        // 16-byte weight pieces per lane and step
     constexpr int BM = 16 * WT;                       // tokens per tile
     constexpr int NO = GEGLU ? WN / 2 : WN;           // output row groups per wave
     constexpr int kStepBytes = BM * kPRowBytes;       // activation tile of one step
@@ -66,11 +71,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     const int64_t tile_n = blockIdx.x / tiles_m;
     const int64_t m0 = (int64_t)tile_m * BM;
     const int64_t o0 = (tile_n * 4 + wave) * (16 * NO);   // first output of this wave
-    const int64_t kb = k / 2;
+    const int64_t kb = k * CB / 8;                    // bytes of a row-major row
     const int64_t kt = (k + 127) / 128;
     const int64_t nsteps = (k + kPBK - 1) / kPBK;
     const int64_t rows = GEGLU ? 2 * n_out : n_out;
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, weight_bytes(TILED, rows, k));
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, code_weight_bytes(CB, TILED, rows, k));
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m * k * 2);
     const uint32_t k32 = (uint32_t)k;
 
@@ -83,8 +88,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
         if (o >= n_out)
             o = n_out - 1;
         const int64_t row = j >= NO ? n_out + o : o;
-        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 + 16 * lane)
-                         : (uint32_t)(row * kb + 16 * g);
+        wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 * WP + 16 * lane)
+                         : (uint32_t)(row * kb + 16 * WP * g);
     }
     // DMA load i of this wave fills LDS bytes [1024 c, 1024 c + 1024) of the
     // step tile, c = XC wave + i: lane l writes token row 4 c + l / 16 at
@@ -126,27 +131,35 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
             buf_load16_lds(xrs, off, &xs[buf][1024 * (XC * wave + i)]);
         }
     };
-    auto load_w = [&](int64_t s, u32x4(&wd)[WN]) {
+    // INT8 codes take two 16-byte loads per row group: the lane's next 16
+    // bytes (row-major) or the tile's second KB (prepacked).
+    auto load_w = [&](int64_t s, u32x4(&wd)[WN][WP]) {
         const uint32_t u = (uint32_t)s * kPBK;
-        const uint32_t step = s < nsteps ? (TILED ? (uint32_t)s * 1024u : u / 2) : kOutOfRange;
+        const uint32_t step = s < nsteps ? (TILED ? (uint32_t)s * 1024u * WP : u * CB / 8) : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
             uint32_t off = wbase[j] + step;
             if (!EVEN && !TILED && u + 32 * g >= k32)
                 off = kOutOfRange;
-            wd[j] = buf_load16(wrs, off);
+#pragma unroll
+            for (int h = 0; h < WP; ++h)
+                wd[j][h] = buf_load16(wrs, off + h * (TILED ? 1024u : 16u));
         }
     };
     // MFMA t of a step covers, for lane group g, reduction indices
     // 32 g + 8 t .. + 7 of the step on both operands.  The WN dequantized
     // A operands stay live while the B operands stream through.
-    auto compute = [&](int buf, const u32x4(&wd)[WN]) {
+    auto compute = [&](int buf, const u32x4(&wd)[WN][WP]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             half8 a[WN];
 #pragma unroll
-            for (int j = 0; j < WN; ++j)
-                a[j] = dequant8_of<TILED>(wd[j][t]);
+            for (int j = 0; j < WN; ++j) {
+                if constexpr (CB == 4)
+                    a[j] = dequant8_of<TILED>(wd[j][0][t]);
+                else
+                    a[j] = dequant8_i8_of<TILED>(wd[j][t / 2][2 * (t % 2)], wd[j][t / 2][2 * (t % 2) + 1]);
+            }
 #pragma unroll
             for (int b = 0; b < WT; ++b) {
                 const half8 bx = as_half8(*reinterpret_cast<const u32x4 *>(
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     // buffer to the other waves while the weight loads stay in flight.
     // The fences order only LDS accesses around the barrier.
     auto publish = [&]() {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WN));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WN * WP));
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
 
     // two register sets for the weights, used alternately (the loop is
     // unrolled twice so no set is ever copied)
-    u32x4 wa[WN], wb[WN];
+    u32x4 wa[WN][WP], wb[WN][WP];
     load_x(0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_w(0, wa);
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     }
 }
 
-template <int WN, int WT, bool GEGLU, bool TILED>
+template <int WN, int WT, bool GEGLU, bool TILED, int CB>
 static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const void *packed,
                                    const void *scales, int64_t n_out, const void *bias, void *y,
                                    hipStream_t stream)
@@ -264,7 +277,7 @@ static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const vo
     const uint16_t *bp = static_cast<const uint16_t *>(bias);
     uint16_t *yp = static_cast<uint16_t *>(y);
 #define W4_PREFILL(EV)                                                                            \
-    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED>), dim3((unsigned)grid),          \
+    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED, CB>), dim3((unsigned)grid),      \
                        dim3(kPThreads), 0, stream, xp, m, k, pp, sp, n_out, bp, yp, (int)tiles_m)
     if (k % kPBK == 0)
         W4_PREFILL(true);
@@ -292,7 +305,7 @@ static int64_t compute_units()
     return cus;
 }
 
-template <bool GEGLU, bool TILED>
+template <bool GEGLU, bool TILED, int CB>
 static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, const void *packed,
                                         const void *scales, int64_t n_out, const void *bias,
                                         void *y, hipStream_t stream)
@@ -311,35 +324,43 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //  * larger plain grids keep 128-token tiles unless they would fill the
     //    last wave of workgroups much worse than 64-token tiles (k <= 16384);
     //  * larger GeGLU grids take 128-token tiles.
+    //  * INT8 codes take 64-token tiles where INT4 takes 128: the second
+    //    weight register set per row group would not fit beside 128 tokens.
+    constexpr int WT = CB == 8 ? 4 : 8;
     constexpr int out_per = 4 * 16 * (GEGLU ? 2 : 4);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
     const int64_t cus = compute_units();
     const int64_t g48 = tiles_n * ((m + 127) / 128);
     if constexpr (GEGLU) {
         if (g48 <= cus)
-            return launch_prefill_t<2, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
-        return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<2, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return launch_prefill_t<4, WT, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
     } else {
         const int64_t slots = 2 * cus;
         const double fill8 = wave_fill(g48, slots);
         if (4 * g48 <= 9 * cus && fill8 < 0.9)
-            return launch_prefill_t<3, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<3, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
         if (k <= 16384 && fill4 > fill8 + 0.1)
-            return launch_prefill_t<4, 4, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
-        return launch_prefill_t<4, 8, GEGLU, TILED>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<4, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return launch_prefill_t<4, WT, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
     }
 }
 
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
                           const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          bool tiled, hipStream_t stream)
+                          bool tiled, int cb, hipStream_t stream)
 {
+#define W4_PLAYOUT(G, T, C) launch_prefill_layout<G, T, C>(x, m, k, packed, scales, n_out, bias, y, stream)
+    if (cb == 8) {
+        if (geglu)
+            return tiled ? W4_PLAYOUT(true, true, 8) : W4_PLAYOUT(true, false, 8);
+        return tiled ? W4_PLAYOUT(false, true, 8) : W4_PLAYOUT(false, false, 8);
+    }
     if (geglu)
-        return tiled ? launch_prefill_layout<true, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                     : launch_prefill_layout<true, false>(x, m, k, packed, scales, n_out, bias, y, stream);
-    return tiled ? launch_prefill_layout<false, true>(x, m, k, packed, scales, n_out, bias, y, stream)
-                 : launch_prefill_layout<false, false>(x, m, k, packed, scales, n_out, bias, y, stream);
+        return tiled ? W4_PLAYOUT(true, true, 4) : W4_PLAYOUT(true, false, 4);
+    return tiled ? W4_PLAYOUT(false, true, 4) : W4_PLAYOUT(false, false, 4);
+#undef W4_PLAYOUT
 }
 
 }  // namespace w4a16

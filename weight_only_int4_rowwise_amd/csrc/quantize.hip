@@ -1,5 +1,7 @@
 // Row-parallel absmax INT4 quantizer for gfx950 (the one-off weight
-// compression step of GLM-130B's weight-only INT4 scheme).
+// compression step of GLM-130B's weight-only INT4 scheme), and its INT8
+// variant (divisor 127, codes in [-127, 127], one two's-complement byte per
+// code: the pages' b-bit scale with b = 8).
 //
 // Per output row r of W fp16 [n][k]  (GLM-130B paper card, "Method"
 // pseudocode and "Paper vs code", bullet "Quantization scale"):
@@ -26,7 +28,12 @@
 // half-integer, while an exact tie is a multiple of 2^-12.  So rounding r
 // to the nearest multiple of 2^-12 returns Q itself for a tie and stays on
 // Q's side of every half-integer otherwise, and rounding that to an
-// integer, ties to even, gives round_half_even(Q).
+// integer, ties to even, gives round_half_even(Q).  The gap holds for any
+// |Q| (the two sides differ by an integer multiple of the significand
+// spacing), so the INT8 codes follow the same steps: there |Q| < 191
+// (subnormal scales included), r is within 2^-15 of Q, and adding
+// 2^23 + 256 leaves q + 256 in the low mantissa bits, whose low byte is
+// q's two's complement.
 #include "common.hpp"
 
 namespace w4a16 {
@@ -59,10 +66,11 @@ struct RowScale {
     uint16_t bits;
 };
 
+template <int QMAX>
 __device__ __forceinline__ RowScale make_scale(uint32_t amax_bits)
 {
     const float a = half_bits_to_float((uint16_t)amax_bits);
-    const uint16_t sb = float_to_half_bits(__fdiv_rn(a, 7.0f));
+    const uint16_t sb = float_to_half_bits(__fdiv_rn(a, (float)QMAX));
     RowScale rs;
     rs.bits = sb;
     rs.s = half_bits_to_float(sb);
@@ -84,9 +92,37 @@ __device__ __forceinline__ uint32_t code_nibble_f(float wf, float inv)
     return __builtin_bit_cast(uint32_t, __fadd_rn(c, 8388624.0f)) & 0xFu;
 }
 
+// Two's-complement byte of the INT8 code of one weight: the same steps
+// with the clamp at 127 and 2^23 + 256 as the rounding constant.
+__device__ __forceinline__ uint32_t code_byte_f(float wf, float inv)
+{
+    const float r = wf * inv;
+    const float snap = __fsub_rn(__fadd_rn(r, 3072.0f), 3072.0f);
+    const float c = __builtin_amdgcn_fmed3f(snap, -127.0f, 127.0f);
+    return __builtin_bit_cast(uint32_t, __fadd_rn(c, 8388864.0f)) & 0xFFu;
+}
+
 __device__ __forceinline__ uint32_t code_nibble(uint32_t wbits, const RowScale &rs)
 {
     return code_nibble_f(half_bits_to_float((uint16_t)wbits), rs.inv);
+}
+
+__device__ __forceinline__ uint32_t code_byte(uint32_t wbits, const RowScale &rs)
+{
+    return code_byte_f(half_bits_to_float((uint16_t)wbits), rs.inv);
+}
+
+// Eight INT8 codes of one 16-byte chunk as two dwords (element e in byte
+// e % 4 of dword e / 4).
+__device__ __forceinline__ uint2 bytes_chunk(u32x4 v, float inv)
+{
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[j / 2] |= code_byte_f(half_bits_to_float((uint16_t)(v[j] & 0xFFFFu)), inv) << (16 * (j % 2));
+        o[j / 2] |= code_byte_f(half_bits_to_float((uint16_t)(v[j] >> 16)), inv) << (16 * (j % 2) + 8);
+    }
+    return uint2{o[0], o[1]};
 }
 
 // Eight codes of one 16-byte chunk (4 dwords of fp16 pairs) as one packed
@@ -106,7 +142,7 @@ __device__ __forceinline__ uint32_t pack_chunk(u32x4 v, float inv)
 // (rows of up to 512 WPR CH halves).  Chunk c of wave part p of the row is
 // chunk (c WPR + p) 64 + lane, so every load and store instruction covers
 // consecutive memory.  Requires k % 8 == 0.
-template <int WPR, int CH>
+template <int WPR, int CH, int QMAX>
 __global__ __launch_bounds__(kQThreads) void quantize_rows_reg(const uint16_t *__restrict__ w,
                                                                int64_t n, int64_t k,
                                                                uint8_t *__restrict__ packed,
@@ -148,22 +184,33 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_reg(const uint16_t *_
         for (int p = 0; p < WPR; ++p)
             m = max(m, lds4[w0 + p]);
     }
-    const RowScale rs = make_scale(m);
+    const RowScale rs = make_scale<QMAX>(m);
     if (live && part == 0 && lane == 0)
         scales[row] = rs.bits;
     if (!live)
         return;
-    uint32_t *pr = reinterpret_cast<uint32_t *>(packed + row * (k / 2));
+    if constexpr (QMAX == 7) {
+        uint32_t *pr = reinterpret_cast<uint32_t *>(packed + row * (k / 2));
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
-        if (idx < nchunk)
-            pr[idx] = pack_chunk(v[c], rs.inv);
+        for (int c = 0; c < CH; ++c) {
+            const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+            if (idx < nchunk)
+                pr[idx] = pack_chunk(v[c], rs.inv);
+        }
+    } else {
+        uint2 *pr = reinterpret_cast<uint2 *>(packed + row * k);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+            if (idx < nchunk)
+                pr[idx] = bytes_chunk(v[c], rs.inv);
+        }
     }
 }
 
 // General path (any even k, any row length): two sweeps over the row; the
 // second one mostly hits in cache.
+template <int QMAX>
 __global__ __launch_bounds__(kQThreads) void quantize_rows_generic(const uint16_t *__restrict__ w,
                                                                    int64_t k,
                                                                    uint8_t *__restrict__ packed,
@@ -172,7 +219,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_generic(const uint16_
     __shared__ uint32_t lds4[4];
     const int64_t row = blockIdx.x;
     const uint16_t *wr = w + row * k;
-    uint8_t *pr = packed + row * (k / 2);
+    uint8_t *pr = packed + row * (QMAX == 7 ? k / 2 : k);
     const int64_t npair = k / 2;
     const uint32_t *wr2 = reinterpret_cast<const uint32_t *>(wr);   // k even: 4-byte pairs
 
@@ -183,17 +230,22 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_generic(const uint16_
         m = max(m, (p >> 16) & 0x7FFFu);
     }
     const uint32_t amax = block_max_u32(m, lds4);
-    const RowScale rs = make_scale(amax);
+    const RowScale rs = make_scale<QMAX>(amax);
     if (threadIdx.x == 0)
         scales[row] = rs.bits;
     for (int64_t i = threadIdx.x; i < npair; i += kQThreads) {
         const uint32_t p = wr2[i];
-        pr[i] = (uint8_t)(code_nibble(p & 0xFFFFu, rs) | (code_nibble(p >> 16, rs) << 4));
+        if constexpr (QMAX == 7)
+            pr[i] = (uint8_t)(code_nibble(p & 0xFFFFu, rs) | (code_nibble(p >> 16, rs) << 4));
+        else
+            reinterpret_cast<uint16_t *>(pr)[i] =
+                (uint16_t)(code_byte(p & 0xFFFFu, rs) | (code_byte(p >> 16, rs) << 8));
     }
 }
 
-hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
-                           hipStream_t stream)
+template <int QMAX>
+static hipError_t launch_quantize_q(const void *w, int64_t n, int64_t k, void *packed, void *scales,
+                                    hipStream_t stream)
 {
     const uint16_t *wp = static_cast<const uint16_t *>(w);
     uint8_t *pp = static_cast<uint8_t *>(packed);
@@ -201,7 +253,7 @@ hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, vo
     // lanes' chunks per row: at most 16 per lane, spread over 1, 2 or 4 waves
     const int64_t lane_chunks = (k / 8 + kWave - 1) / kWave;
 #define W4_QREG(WPR, CH)                                                                           \
-    hipLaunchKernelGGL((quantize_rows_reg<WPR, CH>),                                               \
+    hipLaunchKernelGGL((quantize_rows_reg<WPR, CH, QMAX>),                                         \
                        dim3((unsigned)((n + (4 / WPR) - 1) / (4 / WPR))), dim3(kQThreads), 0,       \
                        stream, wp, n, k, pp, sp)
     if (k % 8 == 0 && lane_chunks <= 64) {
@@ -224,11 +276,23 @@ hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, vo
         else
             W4_QREG(4, 16);
     } else {
-        hipLaunchKernelGGL(quantize_rows_generic, dim3((unsigned)n), dim3(kQThreads), 0, stream,
-                           wp, k, pp, sp);
+        hipLaunchKernelGGL(quantize_rows_generic<QMAX>, dim3((unsigned)n), dim3(kQThreads), 0,
+                           stream, wp, k, pp, sp);
     }
 #undef W4_QREG
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
+                           hipStream_t stream)
+{
+    return launch_quantize_q<7>(w, n, k, packed, scales, stream);
+}
+
+hipError_t launch_quantize_int8(const void *w, int64_t n, int64_t k, void *codes, void *scales,
+                                hipStream_t stream)
+{
+    return launch_quantize_q<127>(w, n, k, codes, scales, stream);
 }
 
 }  // namespace w4a16

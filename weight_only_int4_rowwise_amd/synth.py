@@ -153,16 +153,18 @@ def enumeration_rows(absmax_bits, k: int) -> torch.Tensor:
     return val.to(torch.int16).view(torch.float16)
 
 
-def exponent_rows(n: int, k: int, gen: torch.Generator, e_lo: int = -8, e_hi: int = 0) -> torch.Tensor:
-    """Rows whose absmax is 7 * 2^e (e drawn in [e_lo, e_hi]), with every
-    other entry an integer j * 2^e or (j + 1/2) * 2^e, |j| <= 6: exact
-    power-of-two grids that hit every rounding tie."""
+def exponent_rows(n: int, k: int, gen: torch.Generator, e_lo: int = -8, e_hi: int = 0,
+                  top: int = 7) -> torch.Tensor:
+    """Rows whose absmax is top * 2^e (e drawn in [e_lo, e_hi]), with every
+    other entry an integer j * 2^e or (j + 1/2) * 2^e, |j| < top: exact
+    power-of-two grids that hit every rounding tie (top = 7 for the INT4
+    code range, 127 for INT8)."""
     e = torch.randint(e_lo, e_hi + 1, (n, 1), generator=gen)
-    half_steps = torch.randint(-13, 14, (n, k), generator=gen).to(torch.float64)
+    half_steps = torch.randint(-(2 * top - 1), 2 * top, (n, k), generator=gen).to(torch.float64)
     vals = half_steps * 0.5 * torch.pow(2.0, e.to(torch.float64))
     col = torch.randint(0, k, (n,), generator=gen)
     sign = torch.where(torch.rand(n, generator=gen) < 0.5, -1.0, 1.0).to(torch.float64)
-    vals[torch.arange(n), col] = 7.0 * torch.pow(2.0, e[:, 0].to(torch.float64)) * sign
+    vals[torch.arange(n), col] = float(top) * torch.pow(2.0, e[:, 0].to(torch.float64)) * sign
     return vals.to(torch.float16)
 
 
