@@ -96,6 +96,26 @@ def make_rotating(torch, w4, synth, n, k, dist, count, seed0, dev):
     return qs
 
 
+def make_rotating8(torch, w4, synth, n, k, dist, count, seed0, dev):
+    """count independently drawn weights in INT8: (prepacked codes, scales)."""
+    qs = []
+    for i in range(count):
+        g = synth.generator(seed0 + i, dev)
+        w = synth.weight(n, k, g, dist, dev)
+        q, s = w4.quantize_rowwise_int8(w)
+        del w
+        qs.append((w4.w8a16_prepack(q), s))
+        del q
+    torch.cuda.synchronize()
+    return qs
+
+
+def linear_bytes8(m, n_rows, k, n_out):
+    """Algorithmic bytes of one INT8 linear call: codes n k, fp16 scales,
+    activations in, outputs out."""
+    return n_rows * k + 2 * n_rows + 2 * m * k + 2 * m * n_out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +375,8 @@ def extra_workloads(torch, w4, synth, dev, a):
     log(f"prefill M=512: {pf5}")
     del ups, attn
 
+    res["w8a16"] = int8_workloads(torch, w4, synth, dev, g)
+
     # quantizer: QKV-shaped fp16 weight -> packed + scales
     log("quantizer")
     wq = synth.weight(synth.QKV_OUT, H, g, device=dev)
@@ -373,13 +395,84 @@ def extra_workloads(torch, w4, synth, dev, a):
         # layout the pages serve INT4 with): the same step on the shard shapes
         res["full_decode_step_m8_tp4_shard"] = full_step(torch, w4, synth, dev, synth.shard_linears(4),
                                                          "70-layer decode step, 4-way shard")
+        res["w8a16"]["full_decode_step_m8"] = full_step(torch, w4, synth, dev, synth.LAYER_LINEARS,
+                                                        "INT8 70-layer decode step", cb=8)
     return res
 
 
-def full_step(torch, w4, synth, dev, linears, label):
+def int8_workloads(torch, w4, synth, dev, g):
+    """The INT8 row-wise variant (W8A16) at the GLM-130B shapes: QKV decode
+    per M, the fused GeGLU up-projection and down at M = 1 and 16, and the
+    attention-out prefill at M = 2048, all prepacked."""
+    log("INT8 (W8A16) workloads")
+    H, F, N = synth.HIDDEN, synth.FFN, synth.QKV_OUT
+    r = {}
+    qkv = make_rotating8(torch, w4, synth, N, H, "normal", 3, 500, dev)
+    per_m = {}
+    for m in DECODE_MS:
+        x = synth.activations(m, H, g, dev)
+        y = torch.empty(m, N, dtype=torch.float16, device=dev)
+        c = [0]
+
+        def one(c=c, x=x, y=y):
+            qp, s = qkv[c[0] % len(qkv)]
+            c[0] += 1
+            w4.w8a16_linear_prepacked(x, qp, s, y_out=y)
+
+        t = time_launches(torch, one, 30)
+        b = linear_bytes8(m, N, H, N)
+        per_m[str(m)] = {"us": round(t * 1e6, 2), "bytes": b, "GBs": round(b / t / 1e9, 1),
+                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+    r["decode_qkv_per_m"] = per_m
+    log(f"INT8 QKV decode: {per_m}")
+    del qkv
+    ups = make_rotating8(torch, w4, synth, 2 * F, H, "t4", 2, 600, dev)
+    downs = make_rotating8(torch, w4, synth, H, F, "t4", 3, 700, dev)
+    gd = {}
+    for m in (1, 16):
+        xu = synth.activations(m, H, g, dev)
+        xd = synth.activations(m, F, g, dev)
+        yu = torch.empty(m, F, dtype=torch.float16, device=dev)
+        yd = torch.empty(m, H, dtype=torch.float16, device=dev)
+        c = [0]
+
+        def up(c=c, xu=xu, yu=yu):
+            qp, s = ups[c[0] % len(ups)]
+            c[0] += 1
+            w4.w8a16_geglu_linear_prepacked(xu, qp, s, y_out=yu)
+
+        def down(c=c, xd=xd, yd=yd):
+            qp, s = downs[c[0] % len(downs)]
+            c[0] += 1
+            w4.w8a16_linear_prepacked(xd, qp, s, y_out=yd)
+
+        tu = time_launches(torch, up, 20)
+        td = time_launches(torch, down, 20)
+        bu = linear_bytes8(m, 2 * F, H, F)
+        bd = linear_bytes8(m, H, F, H)
+        gd[str(m)] = {"up_geglu_us": round(tu * 1e6, 2), "up_geglu_GBs": round(bu / tu / 1e9, 1),
+                      "down_us": round(td * 1e6, 2), "down_GBs": round(bd / td / 1e9, 1)}
+    r["decode_geglu_ffn"] = gd
+    log(f"INT8 GeGLU decode: {gd}")
+    del ups, downs
+    attn = make_rotating8(torch, w4, synth, H, H, "normal", 1, 800, dev)
+    M = synth.SEQ
+    x = synth.activations(M, H, g, dev)
+    y = torch.empty(M, H, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.w8a16_linear_prepacked(x, attn[0][0], attn[0][1], y_out=y), 10)
+    fl = 2.0 * M * H * H
+    r["prefill_m2048_attn_out"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                                   "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    log(f"INT8 prefill: {r['prefill_m2048_attn_out']}")
+    del attn, x, y
+    torch.cuda.empty_cache()
+    return r
+
+
+def full_step(torch, w4, synth, dev, linears, label, cb=4):
     """70 layers x the four linears of `linears` (name, rows, k) at M = 8,
-    all weights resident and prepacked, launched back to back on one
-    stream."""
+    all weights resident and prepacked (INT4, or INT8 for cb = 8), launched
+    back to back on one stream."""
     log(f"{label}: generating and quantizing {synth.LAYERS * len(linears)} matrices")
     layers = []
     for l in range(synth.LAYERS):
@@ -387,9 +480,14 @@ def full_step(torch, w4, synth, dev, linears, label):
         for mid, (name, n, k) in enumerate(linears):
             g = synth.generator(synth.layer_weight_seed(l, mid), dev)
             w = synth.weight(n, k, g, device=dev)
-            q, s = w4.quantize_rowwise_int4(w)
-            del w
-            mats.append((w4.w4a16_prepack(q), s))
+            if cb == 8:
+                q, s = w4.quantize_rowwise_int8(w)
+                del w
+                mats.append((w4.w8a16_prepack(q), s))
+            else:
+                q, s = w4.quantize_rowwise_int4(w)
+                del w
+                mats.append((w4.w4a16_prepack(q), s))
             del q
         layers.append(mats)
     torch.cuda.synchronize()
@@ -401,9 +499,13 @@ def full_step(torch, w4, synth, dev, linears, label):
     for name, n, k in linears:
         geglu = name == "ffn_up"
         out = n // 2 if geglu else n
-        fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+        if cb == 8:
+            fn = w4.w8a16_geglu_linear_prepacked if geglu else w4.w8a16_linear_prepacked
+            total += linear_bytes8(M, n, k, out)
+        else:
+            fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+            total += linear_bytes(M, n, k, out)
         calls.append((fn, xs[k], torch.empty(M, out, dtype=torch.float16, device=dev)))
-        total += linear_bytes(M, n, k, out)
     total *= synth.LAYERS
 
     def run():

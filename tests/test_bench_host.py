@@ -58,3 +58,10 @@ def test_shard_linears_split_each_layer_evenly(tp):
         assert n * k * tp == fn * fk
         assert (n == fn // tp and k == fk) if name in ("qkv", "ffn_up") else (n == fn and k == fk // tp)
     assert shard["ffn_up"][0] % 2 == 0
+
+
+def test_int8_bytes_count_one_byte_per_code():
+    """INT8 QKV 36864 x 12288 at M = 1: codes n k, scales 2 n, x 2 m k, y 2 m n."""
+    n, k, m = 36864, 12288, 1
+    assert bench.linear_bytes8(m, n, k, n) == n * k + 2 * n + 2 * m * k + 2 * m * n == 453_156_864
+    assert bench.linear_bytes8(m, n, k, n) - bench.linear_bytes(m, n, k, n) == n * k // 2
