@@ -1,5 +1,6 @@
 """CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear,
-and for the INT8 row-wise variant (W8A16: divisor 127, one code per byte).
+for the INT8 row-wise variant (W8A16: divisor 127, one code per byte), and for
+the zero-point INT4 variant (min/max range, 15 steps, integer zero point).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only users.  The GPU library never imports, links or
@@ -82,6 +83,10 @@ def _load():
         lib.oracle_linear_int8_at.argtypes = [P, I, P, P, P, P, P, I, P, P]
         lib.oracle_geglu_int8.argtypes = [P, I, I, P, P, I, P, P, P, P, P, P]
         lib.oracle_geglu_int8_at.argtypes = [P, I, P, P, I, P, P, P, I, P, P, P, P, P]
+        lib.oracle_quantize_codes_zp.argtypes = [P, I, I, P, P, P]
+        lib.oracle_quantize_rowwise_int4_zp.argtypes = [P, I, I, P, P, P]
+        lib.oracle_linear_zp.argtypes = [P, I, I, P, P, P, I, P, P, P]
+        lib.oracle_geglu_zp.argtypes = [P, I, I, P, P, P, I, P, P, P, P, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -319,6 +324,66 @@ def geglu_int8_at(x, codes, scales, mi, ni, bias=None):
     outs = [np.empty(mi.shape, dtype=np.float64) for _ in range(5)]
     _check(_load().oracle_geglu_int8_at(_ptr(x), k, _ptr(codes), _ptr(scales), f, _ptr(b),
                                         _ptr(mi), _ptr(ni), mi.size, *[_ptr(o) for o in outs]))
+    return tuple(outs)
+
+
+# ------------------------------------------------------ zero-point INT4
+
+def quantize_codes_zp(w):
+    """W fp16 [n][k] -> (codes uint8 [n][k] in [0, 15], scale bits uint16 [n], zero points uint8 [n])."""
+    w = _bits16(w)
+    n, k = w.shape
+    codes = np.empty((n, k), dtype=np.uint8)
+    scales = np.empty(n, dtype=np.uint16)
+    zeros = np.empty(n, dtype=np.uint8)
+    _check(_load().oracle_quantize_codes_zp(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(zeros)))
+    return codes, scales, zeros
+
+
+def quantize_rowwise_int4_zp(w):
+    """W fp16 [n][k] -> (packed uint8 [n][k/2], scale bits uint16 [n], zero points uint8 [n])."""
+    w = _bits16(w)
+    n, k = w.shape
+    packed = np.empty((n, k // 2), dtype=np.uint8)
+    scales = np.empty(n, dtype=np.uint16)
+    zeros = np.empty(n, dtype=np.uint8)
+    _check(_load().oracle_quantize_rowwise_int4_zp(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(zeros)))
+    return packed, scales, zeros
+
+
+def linear_zp(x, packed, scales, zeros, bias=None):
+    """y = x . (s*(q - z))^T (+ bias) in binary64.  Returns (y, mag)."""
+    x = _bits16(x)
+    m, k = x.shape
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = _bits16(scales)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k or scales.shape[0] != n or zeros.shape[0] != n:
+        raise ValueError("shape mismatch")
+    b = None if bias is None else _bits16(bias)
+    y = np.empty((m, n), dtype=np.float64)
+    mag = np.empty((m, n), dtype=np.float64)
+    _check(_load().oracle_linear_zp(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(zeros), n,
+                                    _ptr(b), _ptr(y), _ptr(mag)))
+    return y, mag
+
+
+def geglu_zp(x, packed, scales, zeros, bias=None):
+    """GeGLU over zero-point codes [2f][k/2].  Returns (g, a, b, mag_a, mag_b)."""
+    x = _bits16(x)
+    m, k = x.shape
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = _bits16(scales)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    two_f = packed.shape[0]
+    if two_f % 2 or packed.shape[1] * 2 != k or scales.shape[0] != two_f or zeros.shape[0] != two_f:
+        raise ValueError("shape mismatch")
+    f = two_f // 2
+    b = None if bias is None else _bits16(bias)
+    outs = [np.empty((m, f), dtype=np.float64) for _ in range(5)]
+    _check(_load().oracle_geglu_zp(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(zeros), f,
+                                   _ptr(b), *[_ptr(o) for o in outs]))
     return tuple(outs)
 
 

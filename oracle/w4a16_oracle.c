@@ -1,6 +1,7 @@
 /*
  * CPU oracle for weight-only INT4 row-wise quantization and the W4A16 linear,
- * and for its INT8 row-wise variant (W8A16).
+ * for its INT8 row-wise variant (W8A16), and for the zero-point INT4 variant
+ * that the pages compare it with.
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only callers.  Nothing in the GPU
@@ -21,6 +22,7 @@
  *  [pl-4]     paperlayer.ai summary, "INT4 Quantization for RTX 3090s/2080s"
  *             (weights converted back to FP16 at run time, FP16 activations).
  *  [pl-B3]    paperlayer.ai summary, section B.3 (GeGLU feed-forward).
+ *  [card-P]   wikillm.com paper card, section "Pitfalls" (zero-point INT4 variant).
  * Readings of points the pages leave open are listed beside each function.
  */
 #include <fenv.h>
@@ -490,6 +492,182 @@ int oracle_geglu_int8_at(const uint16_t *x, int64_t k, const int8_t *codes,
         if (mag_a) mag_a[t] = ma;
         if (mag_b) mag_b[t] = mb;
     }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Zero-point INT4 variant                                                 */
+/* [card-P] ("Pitfalls", the row-wise absmax bullet) reports a zero-point   */
+/* INT4 variant at 80.63% LAMBADA against 79.47% for absmax, and that      */
+/* absmax was chosen as the cheaper of the two; the pages give no formula. */
+/* Reading (the standard asymmetric b-bit quantizer, b = 4, 2^b - 1 = 15   */
+/* steps), per output row:                                                 */
+/*   lo = min(min_k W[k], 0),  hi = max(max_k W[k], 0)                      */
+/*   s  = fp16(RNE((hi - lo) / 15))                (stored in FP16)        */
+/*   z  = clamp(RNE(-lo / s), 0, 15)               (integer zero point)    */
+/*   q  = clamp(RNE(W[k] / s) + z, 0, 15)          (unsigned 4-bit code)   */
+/*   W_hat = s * (q - z)                                                    */
+/* The range is widened to hold 0 so that z is an integer in [0, 15];      */
+/* quotients are exact, ties to even; a row whose scale is 0 gets z = 0    */
+/* and all-zero codes.  Codes are packed as the INT4 ones (element 2j low  */
+/* nibble, 2j+1 high), as unsigned nibbles; zero points are uint8 [n].     */
+/* ---------------------------------------------------------------------- */
+
+static int quantize_row_zp(const uint16_t *w, int64_t k, uint8_t *q, uint16_t *s_out,
+                           uint8_t *z_out)
+{
+    double lo = 0.0, hi = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double v = oracle_half_to_double(w[i]);
+        if (!isfinite(v))
+            return ORACLE_ERR_NONFINITE;
+        if (v < lo)
+            lo = v;
+        if (v > hi)
+            hi = v;
+    }
+    /* hi - lo is exact in binary64 (both are binary16 values) */
+    uint16_t s_bits = oracle_double_to_half((hi - lo) / 15.0);
+    double s = oracle_half_to_double(s_bits);
+    double z = 0.0;
+    if (s != 0.0) {
+        z = nearbyint(-lo / s);
+        if (z > 15.0)
+            z = 15.0;
+        if (z < 0.0)
+            z = 0.0;
+    }
+    for (int64_t i = 0; i < k; ++i) {
+        double c = 0.0;
+        if (s != 0.0) {
+            c = nearbyint(oracle_half_to_double(w[i]) / s) + z;
+            if (c > 15.0)
+                c = 15.0;
+            if (c < 0.0)
+                c = 0.0;
+        }
+        q[i] = (uint8_t)c;
+    }
+    *s_out = s_bits;
+    *z_out = (uint8_t)z;
+    return ORACLE_OK;
+}
+
+/* Unpacked codes: W fp16 [n][k] -> codes uint8 [n][k] in [0, 15], scales, zero points. */
+int oracle_quantize_codes_zp(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
+                             uint16_t *scales, uint8_t *zeros)
+{
+    if (!w || !codes || !scales || !zeros || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (check_fe())
+        return ORACLE_ERR_ROUNDING;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < n; ++r) {
+        int st = quantize_row_zp(w + r * k, k, codes + r * k, scales + r, zeros + r);
+        if (st) {
+#pragma omp atomic write
+            status = st;
+        }
+    }
+    return status;
+}
+
+/* Packed: W fp16 [n][k] -> packed [n][k/2] (unsigned nibbles), scales, zero points. */
+int oracle_quantize_rowwise_int4_zp(const uint16_t *w, int64_t n, int64_t k, uint8_t *packed,
+                                    uint16_t *scales, uint8_t *zeros)
+{
+    if (!w || !packed || !scales || !zeros || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+    if (check_fe())
+        return ORACLE_ERR_ROUNDING;
+    int status = ORACLE_OK;
+#pragma omp parallel
+    {
+        uint8_t *q = (uint8_t *)malloc((size_t)k);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n; ++r) {
+            if (!q) {
+#pragma omp atomic write
+                status = ORACLE_ERR_ARG;
+                continue;
+            }
+            int st = quantize_row_zp(w + r * k, k, q, scales + r, zeros + r);
+            if (st) {
+#pragma omp atomic write
+                status = st;
+                continue;
+            }
+            for (int64_t j = 0; j < k / 2; ++j)
+                packed[r * (k / 2) + j] = (uint8_t)((q[2 * j] & 0x0f) | ((q[2 * j + 1] & 0x0f) << 4));
+        }
+        free(q);
+    }
+    return status;
+}
+
+/* One output over zero-point codes: W_hat[k] = s * (q[k] - z); products exact in binary64. */
+static void linear_one_zp(const uint16_t *xrow, int64_t k, const uint8_t *prow, uint16_t s_bits,
+                          uint8_t z, const uint16_t *bias_n, double *y, double *mag)
+{
+    double s = oracle_half_to_double(s_bits);
+    double acc = 0.0, m = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        int u = (i & 1) ? (prow[i / 2] >> 4) : (prow[i / 2] & 0x0f);
+        double t = oracle_half_to_double(xrow[i]) * (s * (double)(u - (int)z));
+        acc += t;
+        m += fabs(t);
+    }
+    if (bias_n) {
+        double b = oracle_half_to_double(*bias_n);
+        acc += b;
+        m += fabs(b);
+    }
+    *y = acc;
+    if (mag)
+        *mag = m;
+}
+
+int oracle_linear_zp(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
+                     const uint16_t *scales, const uint8_t *zeros, int64_t n, const uint16_t *bias,
+                     double *y, double *mag)
+{
+    if (!x || !packed || !scales || !zeros || !y || m < 0 || n < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            linear_one_zp(x + i * k, k, packed + j * (k / 2), scales[j], zeros[j],
+                          bias ? bias + j : NULL, y + i * n + j, mag ? mag + i * n + j : NULL);
+    return ORACLE_OK;
+}
+
+int oracle_geglu_zp(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
+                    const uint16_t *scales, const uint8_t *zeros, int64_t f, const uint16_t *bias,
+                    double *g, double *a_out, double *b_out, double *mag_a, double *mag_b)
+{
+    if (!x || !packed || !scales || !zeros || !g || m < 0 || f < 0 || k <= 0)
+        return ORACLE_ERR_ARG;
+    if (k % 2)
+        return ORACLE_ERR_ODD_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < f; ++j) {
+            double a, b, ma, mb;
+            linear_one_zp(x + i * k, k, packed + j * (k / 2), scales[j], zeros[j],
+                          bias ? bias + j : NULL, &a, &ma);
+            linear_one_zp(x + i * k, k, packed + (f + j) * (k / 2), scales[f + j], zeros[f + j],
+                          bias ? bias + f + j : NULL, &b, &mb);
+            g[i * f + j] = oracle_gelu(a) * b;
+            if (a_out) a_out[i * f + j] = a;
+            if (b_out) b_out[i * f + j] = b;
+            if (mag_a) mag_a[i * f + j] = ma;
+            if (mag_b) mag_b[i * f + j] = mb;
+        }
     return ORACLE_OK;
 }
 

@@ -431,3 +431,152 @@ def test_int8_geglu_vs_numpy_halves(oracle_mod):
     mi = np.array([0, 2, 1]); ni = np.array([0, 47, 20])
     gs = oracle_mod.geglu_int8_at(x, q, s, mi, ni)
     assert np.array_equal(gs[0], gg[mi, ni])
+
+
+# ------------------------------------------------------- zero-point INT4
+# Reading of the pages' zero-point comparison (paper card, "Pitfalls"): the
+# standard asymmetric 4-bit quantizer over [min(w, 0), max(w, 0)], 15 steps,
+# integer zero point.
+
+def _nearest_int(v: Fraction) -> int:
+    """Nearest integer to v, ties to even, by exact comparison."""
+    f = v.numerator // v.denominator
+    d = v - f
+    if d > Fraction(1, 2) or (d == Fraction(1, 2) and f % 2):
+        return f + 1
+    return f
+
+
+def _zp_reference(row):
+    """(s bits, z, codes) of one row from the definition, in exact rationals."""
+    vals = [Fraction(float(v)) for v in row]
+    lo, hi = min(min(vals), Fraction(0)), max(max(vals), Fraction(0))
+    sb = _nearest_fp16_exact((hi - lo) / 15)
+    s = Fraction(float(_f16(sb)))
+    if s == 0:
+        return sb, 0, [0] * len(vals)
+    z = min(15, max(0, _nearest_int(-lo / s)))
+    return sb, z, [min(15, max(0, _nearest_int(v / s) + z)) for v in vals]
+
+
+def _zp_grid_rows(n, k, seed):
+    """Rows with lo = -L 2^e and hi = (15 - L) 2^e (so s = 2^e exactly and z = L),
+    other entries on the half-step grid: every one a tie or an exact level."""
+    rng = np.random.default_rng(seed)
+    rows = np.zeros((n, k), dtype=np.float64)
+    for r in range(n):
+        e = int(rng.integers(-8, 1))
+        L = int(rng.integers(0, 16))
+        half = rng.integers(-2 * L, 2 * (15 - L) + 1, size=k)
+        rows[r] = half * 0.5 * 2.0 ** e
+        rows[r, 0] = -L * 2.0 ** e
+        rows[r, 1] = (15 - L) * 2.0 ** e
+    return rows.astype(np.float16)
+
+
+def test_zp_scale_over_all_hi_and_random_ranges(oracle_mod):
+    """s = fp16((hi - lo)/15): every non-negative fp16 hi with lo = 0, and
+    random (lo, hi) pairs, against an exact-rational nearest search."""
+    a = synth.all_finite_nonneg_fp16().numpy()
+    _, s, z = oracle_mod.quantize_codes_zp(np.stack([a, np.zeros_like(a)], axis=1))
+    for i in range(a.size):
+        assert s[i] == _nearest_fp16_exact(Fraction(float(a[i])) / 15), hex(a.view(np.uint16)[i])
+    assert np.all(z == 0)
+    rng = np.random.default_rng(5)
+    lo = -np.abs(rng.standard_normal(3000) * 0.05).astype(np.float16)
+    hi = np.abs(rng.standard_normal(3000) * 0.05).astype(np.float16)
+    _, s2, _ = oracle_mod.quantize_codes_zp(np.stack([lo, hi], axis=1))
+    for i in range(lo.size):
+        exact = (Fraction(float(hi[i])) - Fraction(float(lo[i]))) / 15
+        assert s2[i] == _nearest_fp16_exact(exact)
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "grid", "positive", "negative"])
+def test_zp_codes_against_exact_definition(oracle_mod, kind):
+    g = synth.generator(61)
+    if kind == "normal":
+        w = synth.weight(24, 40, g).numpy()
+    elif kind == "t4":
+        w = synth.weight(24, 40, g, "t4").numpy()
+    elif kind == "grid":
+        w = _zp_grid_rows(24, 40, 3)
+    elif kind == "positive":
+        w = np.abs(synth.weight(24, 40, g).numpy())
+    else:
+        w = -np.abs(synth.weight(24, 40, g).numpy())
+    q, s, z = oracle_mod.quantize_codes_zp(w)
+    for r in range(w.shape[0]):
+        sb, zr, codes = _zp_reference(w[r])
+        assert s[r] == sb and z[r] == zr, (kind, r)
+        assert q[r].tolist() == codes, (kind, r)
+    if kind == "positive":
+        assert np.all(z == 0)
+    if kind == "negative":
+        assert np.all(z == 15)
+
+
+def test_zp_ties_round_before_the_shift(oracle_mod):
+    """lo = -7, hi = 8: s = 1, z = 7 (odd).  Ties round w/s to even, then add z:
+    0.5 -> 0 + 7 = 7 (rounding w/s + z = 7.5 would give 8)."""
+    w = np.array([[-7, 8, 0.5, 1.5, -0.5, -1.5, 2.5, 0]], dtype=np.float16)
+    q, s, z = oracle_mod.quantize_codes_zp(w)
+    assert s[0] == 0x3C00 and z[0] == 7
+    assert q[0].tolist() == [0, 15, 7, 9, 7, 5, 9, 7]
+
+
+def test_zp_invariants_on_workload_shaped_data(oracle_mod):
+    g = synth.generator(67)
+    for dist in ("normal", "t4"):
+        w = synth.weight(256, 1024, g, dist).numpy()
+        q, s, z = oracle_mod.quantize_codes_zp(w)
+        wv = w.astype(np.float64)
+        sv = _f16(s).astype(np.float64)
+        assert q.max() <= 15 and z.max() <= 15
+        wh = sv[:, None] * (q.astype(np.float64) - z[:, None])
+        # no clamp inside the range: the level nearest to w is within s/2
+        unclamped = (q > 0) & (q < 15)
+        assert np.all(np.abs(wv - wh)[unclamped] <= sv[:, None].repeat(w.shape[1], 1)[unclamped] / 2)
+        # the end levels stay within one step of the row's extremes
+        assert np.all(np.abs(wv - wh) <= sv[:, None] * 1.5)
+        # zero is a level: w = 0 decodes to exactly 0
+        wz = w.copy()
+        wz[:, 5] = 0
+        qz, sz, zz = oracle_mod.quantize_codes_zp(wz)
+        assert np.array_equal(qz[:, 5], zz)
+    # all-zero row
+    q0, s0, z0 = oracle_mod.quantize_codes_zp(np.zeros((2, 8), dtype=np.float16))
+    assert np.all(s0 == 0) and np.all(z0 == 0) and np.all(q0 == 0)
+
+
+def test_zp_packing_matches_codes(oracle_mod):
+    g = synth.generator(71)
+    w = synth.weight(32, 128, g, "t4").numpy()
+    q, s, z = oracle_mod.quantize_codes_zp(w)
+    p, s2, z2 = oracle_mod.quantize_rowwise_int4_zp(w)
+    assert np.array_equal(s, s2) and np.array_equal(z, z2)
+    assert np.array_equal(p & 0xF, q[:, 0::2]) and np.array_equal(p >> 4, q[:, 1::2])
+
+
+def test_zp_linear_and_geglu_vs_numpy(oracle_mod):
+    from scipy.stats import norm
+    g = synth.generator(73)
+    n, k = 96, 512
+    w = synth.weight(n, k, g, "t4").numpy()
+    x = synth.activations(5, k, g).numpy()
+    bias = synth.normal_fp16((n,), 0.5, g).numpy()
+    q, s, z = oracle_mod.quantize_codes_zp(w)
+    p, _, _ = oracle_mod.quantize_rowwise_int4_zp(w)
+    wh = _f16(s).astype(np.float64)[:, None] * (q.astype(np.float64) - z[:, None])
+    y, mag = oracle_mod.linear_zp(x, p, s, z, bias)
+    assert np.allclose(y, x.astype(np.float64) @ wh.T + bias.astype(np.float64), rtol=1e-12, atol=1e-13)
+    assert np.allclose(mag, np.abs(x.astype(np.float64)) @ np.abs(wh).T + np.abs(bias.astype(np.float64)),
+                       rtol=1e-12, atol=1e-13)
+    # one-hot activations pick s (q - z) exactly
+    oh = synth.one_hot_activations(list(range(k)), k).numpy()
+    y1, _ = oracle_mod.linear_zp(oh, p, s, z)
+    assert np.array_equal(y1, wh.T)
+    f = n // 2
+    gg, aa, bb, _, _ = oracle_mod.geglu_zp(x, p, s, z)
+    a = x.astype(np.float64) @ wh[:f].T
+    b = x.astype(np.float64) @ wh[f:].T
+    assert np.allclose(gg, a * norm.cdf(a) * b, rtol=1e-11, atol=1e-13)
