@@ -1,5 +1,5 @@
-"""The C-ABI library loads, exports what include/w4a16.h and include/w8a16.h
-declare, and rejects bad arguments before touching any device (runs without
+"""The C-ABI library loads, exports what include/w4a16.h, include/w8a16.h and
+include/w4a16_zp.h declare, and rejects bad arguments before touching any device (runs without
 a GPU)."""
 import ctypes
 import os
@@ -10,7 +10,7 @@ import pytest
 from weight_only_int4_rowwise_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w8a16.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w8a16.h", "w4a16_zp.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libw4a16.so not built (python -m weight_only_int4_rowwise_amd.build)")
@@ -192,3 +192,23 @@ def test_int8_binding_refuses_cpu_tensors():
     import weight_only_int4_rowwise_amd as w4
     with pytest.raises(ValueError, match="no CPU path"):
         w4.quantize_rowwise_int8(torch.zeros(4, 32, dtype=torch.float16))
+
+
+def test_zp_quantize_argument_checks(lib):
+    q = lib.quantize_rowwise_int4_zp
+    assert q(A, 4, 32, B, C, None, None) == _lib.ERR_NULL          # zero points
+    assert q(A, 4, 33, B, C, D, None) == _lib.ERR_SHAPE
+    assert q(A, 4, 32, B, C, MIS, None) == _lib.ERR_ALIGN
+    assert q(None, 0, 32, None, None, None, None) == _lib.OK
+
+
+@pytest.mark.parametrize("fn", ["w4a16_zp_linear", "w4a16_zp_geglu_linear",
+                                "w4a16_zp_linear_prepacked", "w4a16_zp_geglu_linear_prepacked"])
+def test_zp_linear_argument_checks(lib, fn):
+    f = getattr(lib, fn)
+    E = 0x50000
+    assert f(A, 1, 64, B, C, None, 16, None, D, None) == _lib.ERR_NULL     # zero points
+    assert f(A, 1, 64, B, C, MIS, 16, None, D, None) == _lib.ERR_ALIGN
+    assert f(None, 1, 64, B, C, E, 16, None, D, None) == _lib.ERR_NULL
+    assert f(A, 1, 48, B, C, E, 16, None, D, None) == _lib.ERR_SHAPE       # k % 32 != 0
+    assert f(None, 0, 64, None, None, None, 16, None, None, None) == _lib.OK

@@ -21,6 +21,13 @@ b = 8: s = absmax / 127, one int8 code per weight) has the same calls:
     c, s = quantize_rowwise_int8(w)            # c: cuda int8 [n][k]
     y = w8a16_linear(x, c, s)
     y = w8a16_linear_prepacked(x, w8a16_prepack(c), s)
+
+The zero-point INT4 variant (include/w4a16_zp.h; the scheme the pages compare
+absmax with) adds uint8 zero points [n]; w4a16_prepack reorders its codes:
+
+    q, s, z = quantize_rowwise_int4_zp(w)
+    y = w4a16_zp_linear(x, q, s, z)
+    y = w4a16_zp_linear_prepacked(x, w4a16_prepack(q), s, z)
 """
 from __future__ import annotations
 
@@ -42,6 +49,11 @@ __all__ = [
     "w8a16_prepack",
     "w8a16_linear_prepacked",
     "w8a16_geglu_linear_prepacked",
+    "quantize_rowwise_int4_zp",
+    "w4a16_zp_linear",
+    "w4a16_zp_geglu_linear",
+    "w4a16_zp_linear_prepacked",
+    "w4a16_zp_geglu_linear_prepacked",
     "W4A16Error",
     "library",
 ]
@@ -381,4 +393,102 @@ def w8a16_geglu_linear_prepacked(x, qp, s, bias=None, y_out=None):
                  x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), f,
                  None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w8a16_geglu_linear_prepacked")
+    return y_out
+
+
+# --------------------------------------------------------------------------
+# Zero-point INT4 variant (include/w4a16_zp.h)
+# --------------------------------------------------------------------------
+
+def quantize_rowwise_int4_zp(w, q_out=None, s_out=None, z_out=None):
+    """W fp16 [n][k] (k even) -> (packed uint8 [n][k/2] unsigned codes, scales fp16 [n],
+    zero points uint8 [n])."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(w, torch.float16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [out_features][in_features]")
+    n, k = w.shape
+    if q_out is None:
+        q_out = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if s_out is None:
+        s_out = torch.empty((n,), dtype=torch.float16, device=w.device)
+    if z_out is None:
+        z_out = torch.empty((n,), dtype=torch.uint8, device=w.device)
+    _require(q_out, torch.uint8, "q_out")
+    _require(s_out, torch.float16, "s_out")
+    _require(z_out, torch.uint8, "z_out")
+    if tuple(q_out.shape) != (n, k // 2) or tuple(s_out.shape) != (n,) or tuple(z_out.shape) != (n,):
+        raise ValueError("output shape mismatch")
+    dev = w.get_device()
+    for t, nm in ((q_out, "q_out"), (s_out, "s_out"), (z_out, "z_out")):
+        _same_device(t, dev, nm, "quantize_rowwise_int4_zp")
+    st = _launch(lib.quantize_rowwise_int4_zp, dev, w.data_ptr(), n, k, q_out.data_ptr(),
+                 s_out.data_ptr(), z_out.data_ptr())
+    _lib.check(st, "quantize_rowwise_int4_zp")
+    return q_out, s_out, z_out
+
+
+def _zeros_check(z, rows, dev, name):
+    torch = _torch()
+    _require(z, torch.uint8, "z")
+    if z.dim() != 1 or z.shape[0] != rows:
+        raise ValueError(f"{name}: zero points must be uint8 [{rows}]")
+    _same_device(z, dev, "z", name)
+
+
+def w4a16_zp_linear(x, q, s, z, bias=None, y_out=None):
+    """y[m][n] = fp16(s * (x . (q - z)^T) + bias) over zero-point codes."""
+    lib = _lib.load()
+    n = q.shape[0]
+    m, k, y_out = _linear_common(x, q, s, bias, n, n, y_out, "w4a16_zp_linear")
+    _zeros_check(z, n, x.get_device(), "w4a16_zp_linear")
+    st = _launch(lib.w4a16_zp_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), z.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w4a16_zp_linear")
+    return y_out
+
+
+def w4a16_zp_geglu_linear(x, q, s, z, bias=None, y_out=None):
+    """GeGLU over zero-point codes [2f][k/2] with zero points [2f]."""
+    lib = _lib.load()
+    rows = q.shape[0]
+    if rows % 2:
+        raise ValueError("w4a16_zp_geglu_linear: q must have an even number of rows (2f)")
+    f = rows // 2
+    m, k, y_out = _linear_common(x, q, s, bias, f, rows, y_out, "w4a16_zp_geglu_linear")
+    _zeros_check(z, rows, x.get_device(), "w4a16_zp_geglu_linear")
+    st = _launch(lib.w4a16_zp_geglu_linear, x.get_device(),
+                 x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), z.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w4a16_zp_geglu_linear")
+    return y_out
+
+
+def w4a16_zp_linear_prepacked(x, qp, s, z, bias=None, y_out=None):
+    """w4a16_zp_linear with the codes reordered by w4a16_prepack (n = len(s))."""
+    n = s.shape[0]
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, n, n, y_out, "w4a16_zp_linear_prepacked")
+    _zeros_check(z, n, x.get_device(), "w4a16_zp_linear_prepacked")
+    st = _launch(lib.w4a16_zp_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), z.data_ptr(), n,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w4a16_zp_linear_prepacked")
+    return y_out
+
+
+def w4a16_zp_geglu_linear_prepacked(x, qp, s, z, bias=None, y_out=None):
+    """w4a16_zp_geglu_linear with prepacked codes (f = len(s) / 2)."""
+    rows = s.shape[0]
+    if rows % 2:
+        raise ValueError("w4a16_zp_geglu_linear_prepacked: s must have 2f entries")
+    f = rows // 2
+    lib, m, k, y_out = _prepacked_common(x, qp, s, bias, f, rows, y_out,
+                                         "w4a16_zp_geglu_linear_prepacked")
+    _zeros_check(z, rows, x.get_device(), "w4a16_zp_geglu_linear_prepacked")
+    st = _launch(lib.w4a16_zp_geglu_linear_prepacked, x.get_device(),
+                 x.data_ptr(), m, k, qp.data_ptr(), s.data_ptr(), z.data_ptr(), f,
+                 None if bias is None else bias.data_ptr(), y_out.data_ptr())
+    _lib.check(st, "w4a16_zp_geglu_linear_prepacked")
     return y_out

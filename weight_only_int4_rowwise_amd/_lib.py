@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 # Status codes of include/w4a16.h
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_DEVICE = range(6)
 
-# Every symbol include/w4a16.h and include/w8a16.h declare.
+# Every symbol include/w4a16.h, include/w8a16.h and include/w4a16_zp.h declare.
 EXPORTS = (
     "quantize_rowwise_int4",
     "w4a16_linear",
@@ -33,6 +33,11 @@ EXPORTS = (
     "w8a16_prepack",
     "w8a16_linear_prepacked",
     "w8a16_geglu_linear_prepacked",
+    "quantize_rowwise_int4_zp",
+    "w4a16_zp_linear",
+    "w4a16_zp_geglu_linear",
+    "w4a16_zp_linear_prepacked",
+    "w4a16_zp_geglu_linear_prepacked",
 )
 
 ABI_VERSION = 1
@@ -85,6 +90,12 @@ def load() -> ctypes.CDLL:
     lib.w8a16_prepacked_bytes.restype = ctypes.c_int64
     lib.w8a16_prepack.argtypes = [P, I, I, P, P]
     lib.w8a16_prepack.restype = ctypes.c_int
+    lib.quantize_rowwise_int4_zp.argtypes = [P, I, I, P, P, P, P]
+    lib.quantize_rowwise_int4_zp.restype = ctypes.c_int
+    for fn in ("w4a16_zp_linear", "w4a16_zp_geglu_linear", "w4a16_zp_linear_prepacked",
+               "w4a16_zp_geglu_linear_prepacked"):
+        getattr(lib, fn).argtypes = [P, I, I, P, P, P, I, P, P, P]
+        getattr(lib, fn).restype = ctypes.c_int
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_last_error.argtypes = []

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "prefill.hip", "prepack.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_w8.hip", "decode_zp.hip", "prefill.hip",
+           "prepack.hip"]
 ARCH = "gfx950"
 
 
@@ -44,12 +45,26 @@ def compile_flags() -> list[str]:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *(extra or []), "-shared",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object in parallel (the decode launch tables
+    are split over three sources for this), then link the shared library."""
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="w4a16_build_") as tmpdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            cmd = [hipcc(), *compile_flags(), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd)))
+            objs.append(obj)
+        failed = [src for src, p in procs if p.wait() != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, f"hipcc {' '.join(failed)}")
+        tmp = LIB_PATH + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -3,6 +3,7 @@
 // and include/w8a16.h.
 #include "../../include/w4a16.h"
 #include "../../include/w8a16.h"
+#include "../../include/w4a16_zp.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -13,12 +14,14 @@ hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, vo
                            hipStream_t stream);
 hipError_t launch_quantize_int8(const void *w, int64_t n, int64_t k, void *codes, void *scales,
                                 hipStream_t stream);
+hipError_t launch_quantize_zp(const void *w, int64_t n, int64_t k, void *packed, void *scales,
+                              void *zeros, hipStream_t stream);
 hipError_t launch_decode(const void *x, int m, int64_t k, const void *packed, const void *scales,
-                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
-                         hipStream_t stream);
+                         int64_t n_out, const void *bias, const void *zeros, void *y, bool geglu,
+                         bool tiled, int cb, hipStream_t stream);
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
-                          const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          bool tiled, int cb, hipStream_t stream);
+                          const void *scales, int64_t n_out, const void *bias, const void *zeros,
+                          void *y, bool geglu, bool tiled, int cb, hipStream_t stream);
 int64_t prepacked_bytes(int64_t n, int64_t k);
 hipError_t launch_prepack(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
 int64_t prepacked_bytes_int8(int64_t n, int64_t k);
@@ -81,9 +84,10 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
     return W4A16_OK;
 }
 
+// zeros: per-row zero points of the zero-point INT4 variant, or NULL.
 w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, const void *s,
                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
-                        void *stream)
+                        void *stream, const void *zeros = nullptr, bool zp = false)
 {
     const int64_t rows = geglu ? 2 * n_out : n_out;
     w4a16_status st = check_gemm_shape(m, k, rows, tiled, cb);
@@ -94,10 +98,14 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
     st = check_gemm_ptrs(x, q, s, bias, y);
     if (st != W4A16_OK)
         return st;
+    if (zp && !zeros)
+        return W4A16_ERR_NULL;
+    if (zp && !aligned16(zeros))
+        return W4A16_ERR_ALIGN;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (m <= kDecodeMaxM) {
-        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
+        e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, zeros, y, geglu, tiled, cb, hs);
     } else if (m <= 2 * kDecodeMaxM) {
         // 64 < m <= 128: the first 64 tokens, then the rest, each through
         // the decode kernel.  The weights stream twice, but every CU stays
@@ -106,14 +114,15 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
         // attention-out 12288 x 12288 at m = 96: 59 against 83 us).
         // Outputs depend only on their own token row, so the split changes
         // no result bits.
-        e = w4a16::launch_decode(x, (int)kDecodeMaxM, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
+        e = w4a16::launch_decode(x, (int)kDecodeMaxM, k, q, s, n_out, bias, zeros, y, geglu, tiled,
+                                 cb, hs);
         if (e == hipSuccess)
             e = w4a16::launch_decode(static_cast<const uint16_t *>(x) + kDecodeMaxM * k,
-                                     (int)(m - kDecodeMaxM), k, q, s, n_out, bias,
+                                     (int)(m - kDecodeMaxM), k, q, s, n_out, bias, zeros,
                                      static_cast<uint16_t *>(y) + kDecodeMaxM * n_out, geglu,
                                      tiled, cb, hs);
     } else {
-        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, y, geglu, tiled, cb, hs);
+        e = w4a16::launch_prefill(x, m, k, q, s, n_out, bias, zeros, y, geglu, tiled, cb, hs);
     }
     return from_hip(e);
 }
@@ -270,6 +279,59 @@ w4a16_status w8a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t
         return W4A16_ERR_SHAPE;
     return run_linear(x_fp16, m, k, codes_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true,
                       8, stream);
+}
+
+w4a16_status quantize_rowwise_int4_zp(const void *w_fp16, int64_t n, int64_t k, void *q_packed,
+                                      void *scales_fp16, void *zeros_u8, void *stream)
+{
+    if (n < 0 || k < 2 || k % 2 != 0 || n > 0x7FFFFFFF || k > kMaxDim)
+        return W4A16_ERR_SHAPE;
+    if (n == 0)
+        return W4A16_OK;
+    if (!w_fp16 || !q_packed || !scales_fp16 || !zeros_u8)
+        return W4A16_ERR_NULL;
+    if (!aligned16(w_fp16) || !aligned16(q_packed) || !aligned16(scales_fp16) || !aligned16(zeros_u8))
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_quantize_zp(w_fp16, n, k, q_packed, scales_fp16, zeros_u8,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status w4a16_zp_linear(const void *x_fp16, int64_t m, int64_t k, const void *q_packed,
+                             const void *scales_fp16, const void *zeros_u8, int64_t n,
+                             const void *bias_fp16, void *y_fp16, void *stream)
+{
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, n, bias_fp16, y_fp16, false, false, 4,
+                      stream, zeros_u8, true);
+}
+
+w4a16_status w4a16_zp_geglu_linear(const void *x_fp16, int64_t m, int64_t k, const void *q_packed,
+                                   const void *scales_fp16, const void *zeros_u8, int64_t f,
+                                   const void *bias_fp16, void *y_fp16, void *stream)
+{
+    if (f > kMaxDim / 2)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, q_packed, scales_fp16, f, bias_fp16, y_fp16, true, false, 4,
+                      stream, zeros_u8, true);
+}
+
+w4a16_status w4a16_zp_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                       const void *q_prepacked, const void *scales_fp16,
+                                       const void *zeros_u8, int64_t n, const void *bias_fp16,
+                                       void *y_fp16, void *stream)
+{
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, n, bias_fp16, y_fp16, false, true, 4,
+                      stream, zeros_u8, true);
+}
+
+w4a16_status w4a16_zp_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t k,
+                                             const void *q_prepacked, const void *scales_fp16,
+                                             const void *zeros_u8, int64_t f,
+                                             const void *bias_fp16, void *y_fp16, void *stream)
+{
+    if (f > kMaxDim / 2 || f % 16 != 0)
+        return W4A16_ERR_SHAPE;
+    return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true, 4,
+                      stream, zeros_u8, true);
 }
 
 const char *w4a16_status_string(int status)

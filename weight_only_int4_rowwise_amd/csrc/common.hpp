@@ -92,6 +92,55 @@ __device__ __forceinline__ half8 dequant8_of(uint32_t packed)
 }
 
 // ---------------------------------------------------------------------------
+// Zero-point INT4 -> FP16: unsigned codes u in [0, 15] and a per-row zero
+// point z give the exact fp16 integers u - z in [-15, 15].  The bit trick of
+// dequant8 without the sign flip puts 1024 + u (low nibbles) or 64 + u
+// (high nibbles) in a binary16; the packed subtract then takes 1024 + z or
+// 64 + z, held per lane for its row instead of as constants.  Same op count
+// as dequant8 / dequant8_rm.
+// ---------------------------------------------------------------------------
+struct ZBias {
+    half2v lo;   // (1024 + z, 1024 + z): low nibbles, prepacked order
+    half2v hi;   // (64 + z, 64 + z): high nibbles, prepacked order
+    half2v rm;   // (1024 + z, 64 + z): row-major order
+};
+
+__device__ __forceinline__ ZBias make_zbias(uint32_t z)
+{
+    const _Float16 a = (_Float16)(1024.0f + (float)z), b = (_Float16)(64.0f + (float)z);
+    return ZBias{half2v{a, a}, half2v{b, b}, half2v{a, b}};
+}
+
+__device__ __forceinline__ half8 dequant8_zp(uint32_t packed, const ZBias &zb)
+{
+    const uint32_t w8 = packed >> 8;
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, bits_to_h2((packed & 0x000F000Fu) | 0x64006400u) - zb.lo);
+    r[1] = __builtin_bit_cast(uint32_t, bits_to_h2((packed & 0x00F000F0u) | 0x54005400u) - zb.hi);
+    r[2] = __builtin_bit_cast(uint32_t, bits_to_h2((w8 & 0x000F000Fu) | 0x64006400u) - zb.lo);
+    r[3] = __builtin_bit_cast(uint32_t, bits_to_h2((w8 & 0x00F000F0u) | 0x54005400u) - zb.hi);
+    return __builtin_bit_cast(half8, r);
+}
+
+__device__ __forceinline__ half8 dequant8_rm_zp(uint32_t packed, const ZBias &zb)
+{
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t sel = 0x0c000c00u | (uint32_t)i | ((uint32_t)i << 16);
+        const uint32_t b = __builtin_amdgcn_perm(0u, packed, sel);
+        r[i] = __builtin_bit_cast(uint32_t, bits_to_h2((b & 0x00F0000Fu) | 0x54006400u) - zb.rm);
+    }
+    return __builtin_bit_cast(half8, r);
+}
+
+template <bool PREPACKED>
+__device__ __forceinline__ half8 dequant8_zp_of(uint32_t packed, const ZBias &zb)
+{
+    return PREPACKED ? dequant8_zp(packed, zb) : dequant8_rm_zp(packed, zb);
+}
+
+// ---------------------------------------------------------------------------
 // INT8 -> FP16 dequantization of two dwords (8 codes in their natural
 // order) into one MFMA operand.  A code q in [-127, 127] as the offset
 // byte u = q + 128 (q's two's-complement byte with its top bit flipped)

@@ -41,18 +41,20 @@ constexpr int kPBK = 128;                 // reduction step
 constexpr int kPRowBytes = 2 * kPBK;      // bytes of one token row per step
 constexpr int kPThreads = 256;
 
-template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED, int CB>
+template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED, int CB, bool ZP>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *__restrict__ x,
                                                             int64_t m, int64_t k,
                                                             const uint8_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             int64_t n_out,
                                                             const uint16_t *__restrict__ bias,
+                                                            const uint8_t *__restrict__ zeros,
                                                             uint16_t *__restrict__ y,
                                                             int tiles_m)
 {
     static_assert(!GEGLU || WN % 2 == 0, "GeGLU pairs gate and value row groups");
     static_assert(CB == 4 || CB == 8, "INT4 or INT8 codes");
+    static_assert(!ZP || CB == 4, "zero points are an INT4 variant");
     constexpr int WP = CB / 4;                        // 16-byte weight pieces per lane and step
     constexpr int BM = 16 * WT;                       // tokens per tile
     constexpr int NO = GEGLU ? WN / 2 : WN;           // output row groups per wave
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     // per-lane constant part of the weight offsets; row group j is output
     // group j % NO, and for GeGLU j >= NO is the value partner of gate j - NO
     uint32_t wbase[WN];
+    ZBias zb[ZP ? WN : 1];                            // zero-point subtrahends of this lane's rows
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
         int64_t o = o0 + 16 * (j % NO) + r16;
@@ -90,6 +93,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
         const int64_t row = j >= NO ? n_out + o : o;
         wbase[j] = TILED ? (uint32_t)((row >> 4) * kt * 1024 * WP + 16 * lane)
                          : (uint32_t)(row * kb + 16 * WP * g);
+        if constexpr (ZP)
+            zb[j] = make_zbias(zeros[row]);
     }
     // DMA load i of this wave fills LDS bytes [1024 c, 1024 c + 1024) of the
     // step tile, c = XC wave + i: lane l writes token row 4 c + l / 16 at
@@ -155,7 +160,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
             half8 a[WN];
 #pragma unroll
             for (int j = 0; j < WN; ++j) {
-                if constexpr (CB == 4)
+                if constexpr (ZP)
+                    a[j] = dequant8_zp_of<TILED>(wd[j][0][t], zb[j]);
+                else if constexpr (CB == 4)
                     a[j] = dequant8_of<TILED>(wd[j][0][t]);
                 else
                     a[j] = dequant8_i8_of<TILED>(wd[j][t / 2][2 * (t % 2)], wd[j][t / 2][2 * (t % 2) + 1]);
@@ -260,10 +267,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     }
 }
 
-template <int WN, int WT, bool GEGLU, bool TILED, int CB>
+template <int WN, int WT, bool GEGLU, bool TILED, int CB, bool ZP>
 static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const void *packed,
-                                   const void *scales, int64_t n_out, const void *bias, void *y,
-                                   hipStream_t stream)
+                                   const void *scales, int64_t n_out, const void *bias,
+                                   const void *zeros, void *y, hipStream_t stream)
 {
     constexpr int out_per = 4 * 16 * (GEGLU ? WN / 2 : WN);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
@@ -275,10 +282,11 @@ static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const vo
     const uint8_t *pp = static_cast<const uint8_t *>(packed);
     const uint16_t *sp = static_cast<const uint16_t *>(scales);
     const uint16_t *bp = static_cast<const uint16_t *>(bias);
+    const uint8_t *zp = static_cast<const uint8_t *>(zeros);
     uint16_t *yp = static_cast<uint16_t *>(y);
 #define W4_PREFILL(EV)                                                                            \
-    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED, CB>), dim3((unsigned)grid),      \
-                       dim3(kPThreads), 0, stream, xp, m, k, pp, sp, n_out, bp, yp, (int)tiles_m)
+    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED, CB, ZP>), dim3((unsigned)grid),  \
+                       dim3(kPThreads), 0, stream, xp, m, k, pp, sp, n_out, bp, zp, yp, (int)tiles_m)
     if (k % kPBK == 0)
         W4_PREFILL(true);
     else
@@ -305,10 +313,10 @@ static int64_t compute_units()
     return cus;
 }
 
-template <bool GEGLU, bool TILED, int CB>
+template <bool GEGLU, bool TILED, int CB, bool ZP>
 static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, const void *packed,
                                         const void *scales, int64_t n_out, const void *bias,
-                                        void *y, hipStream_t stream)
+                                        const void *zeros, void *y, hipStream_t stream)
 {
     // Tile shape from the grid of the largest tile (4 x 16 x 4 rows x 128
     // tokens; GeGLU 128 outputs x 128 tokens), measured at the GLM-130B
@@ -333,33 +341,39 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     const int64_t g48 = tiles_n * ((m + 127) / 128);
     if constexpr (GEGLU) {
         if (g48 <= cus)
-            return launch_prefill_t<2, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
-        return launch_prefill_t<4, WT, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<2, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        return launch_prefill_t<4, WT, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     } else {
         const int64_t slots = 2 * cus;
         const double fill8 = wave_fill(g48, slots);
         if (4 * g48 <= 9 * cus && fill8 < 0.9)
-            return launch_prefill_t<3, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
         if (k <= 16384 && fill4 > fill8 + 0.1)
-            return launch_prefill_t<4, 4, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
-        return launch_prefill_t<4, WT, GEGLU, TILED, CB>(x, m, k, packed, scales, n_out, bias, y, stream);
+            return launch_prefill_t<4, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        return launch_prefill_t<4, WT, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     }
 }
 
 hipError_t launch_prefill(const void *x, int64_t m, int64_t k, const void *packed,
-                          const void *scales, int64_t n_out, const void *bias, void *y, bool geglu,
-                          bool tiled, int cb, hipStream_t stream)
+                          const void *scales, int64_t n_out, const void *bias, const void *zeros,
+                          void *y, bool geglu, bool tiled, int cb, hipStream_t stream)
 {
-#define W4_PLAYOUT(G, T, C) launch_prefill_layout<G, T, C>(x, m, k, packed, scales, n_out, bias, y, stream)
+#define W4_PLAYOUT(G, T, C, Z)                                                                    \
+    launch_prefill_layout<G, T, C, Z>(x, m, k, packed, scales, n_out, bias, zeros, y, stream)
     if (cb == 8) {
         if (geglu)
-            return tiled ? W4_PLAYOUT(true, true, 8) : W4_PLAYOUT(true, false, 8);
-        return tiled ? W4_PLAYOUT(false, true, 8) : W4_PLAYOUT(false, false, 8);
+            return tiled ? W4_PLAYOUT(true, true, 8, false) : W4_PLAYOUT(true, false, 8, false);
+        return tiled ? W4_PLAYOUT(false, true, 8, false) : W4_PLAYOUT(false, false, 8, false);
+    }
+    if (zeros) {
+        if (geglu)
+            return tiled ? W4_PLAYOUT(true, true, 4, true) : W4_PLAYOUT(true, false, 4, true);
+        return tiled ? W4_PLAYOUT(false, true, 4, true) : W4_PLAYOUT(false, false, 4, true);
     }
     if (geglu)
-        return tiled ? W4_PLAYOUT(true, true, 4) : W4_PLAYOUT(true, false, 4);
-    return tiled ? W4_PLAYOUT(false, true, 4) : W4_PLAYOUT(false, false, 4);
+        return tiled ? W4_PLAYOUT(true, true, 4, false) : W4_PLAYOUT(true, false, 4, false);
+    return tiled ? W4_PLAYOUT(false, true, 4, false) : W4_PLAYOUT(false, false, 4, false);
 #undef W4_PLAYOUT
 }
 

@@ -283,6 +283,114 @@ static hipError_t launch_quantize_q(const void *w, int64_t n, int64_t k, void *p
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Zero-point INT4 variant (the pages' comparison scheme; the formula is the
+// standard asymmetric 4-bit one):
+//   lo = min(min_c W, 0), hi = max(max_c W, 0)
+//   s  = fp16((hi - lo) / 15),  z = clamp(round_half_even(-lo / s), 0, 15)
+//   q  = clamp(round_half_even(W / s) + z, 0, 15)   (unsigned nibbles)
+// One 256-thread workgroup per row, two sweeps (the second hits in cache).
+// Exactness: hi - lo is exact in binary64, the division is correctly
+// rounded, and rounding that to fp32 then fp16 is the correctly rounded fp16
+// quotient (53 -> 24 -> 11 bits: 24 >= 2 * 11 + 2).  -lo / s in binary64 is
+// far closer to the exact quotient than the 2^-12 gap that separates a
+// non-tie quotient from a half-integer, so rint gives its round-half-even.
+// The codes follow the INT4 steps (|w / s| <= 15 here).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t code_zp_f(float wf, float inv, float zf)
+{
+    const float r = wf * inv;
+    const float snap = __fsub_rn(__fadd_rn(r, 3072.0f), 3072.0f);
+    return (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(snap) + zf, 0.0f, 15.0f);
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_rows_zp(const uint16_t *__restrict__ w,
+                                                              int64_t k,
+                                                              uint8_t *__restrict__ packed,
+                                                              uint16_t *__restrict__ scales,
+                                                              uint8_t *__restrict__ zeros)
+{
+    __shared__ float red[2][kQThreads / kWave];
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = w + row * k;
+    uint8_t *pr = packed + row * (k / 2);
+    const bool chunks = k % 8 == 0;                 // 16-byte loads, 4-byte stores
+    const int64_t nchunk = chunks ? k / 8 : k / 2;
+
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t i = threadIdx.x; i < nchunk; i += kQThreads) {
+        if (chunks) {
+            const u32x4 v = load16(wr + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = half_bits_to_float((uint16_t)(v[j] & 0xFFFFu));
+                const float b = half_bits_to_float((uint16_t)(v[j] >> 16));
+                lo = fminf(lo, fminf(a, b));
+                hi = fmaxf(hi, fmaxf(a, b));
+            }
+        } else {
+            const uint32_t p2 = reinterpret_cast<const uint32_t *>(wr)[i];
+            const float a = half_bits_to_float((uint16_t)(p2 & 0xFFFFu));
+            const float b = half_bits_to_float((uint16_t)(p2 >> 16));
+            lo = fminf(lo, fminf(a, b));
+            hi = fmaxf(hi, fmaxf(a, b));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+    }
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        red[0][wave] = lo;
+        red[1][wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kQThreads / kWave; ++i) {
+        lo = fminf(lo, red[0][i]);
+        hi = fmaxf(hi, red[1][i]);
+    }
+    const uint16_t sb = float_to_half_bits((float)(((double)hi - (double)lo) / 15.0));
+    const float s = half_bits_to_float(sb);
+    float inv = 0.0f, zf = 0.0f;
+    if (s != 0.0f) {
+        inv = __fdiv_rn(1.0f, s);
+        zf = (float)__builtin_rint(-(double)lo / (double)s);
+        zf = __builtin_amdgcn_fmed3f(zf, 0.0f, 15.0f);
+    }
+    if (threadIdx.x == 0) {
+        scales[row] = sb;
+        zeros[row] = (uint8_t)zf;
+    }
+    for (int64_t i = threadIdx.x; i < nchunk; i += kQThreads) {
+        if (chunks) {
+            const u32x4 v = load16(wr + 8 * i);
+            uint32_t out = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out |= code_zp_f(half_bits_to_float((uint16_t)(v[j] & 0xFFFFu)), inv, zf) << (8 * j);
+                out |= code_zp_f(half_bits_to_float((uint16_t)(v[j] >> 16)), inv, zf) << (8 * j + 4);
+            }
+            reinterpret_cast<uint32_t *>(pr)[i] = out;
+        } else {
+            const uint32_t p2 = reinterpret_cast<const uint32_t *>(wr)[i];
+            pr[i] = (uint8_t)(code_zp_f(half_bits_to_float((uint16_t)(p2 & 0xFFFFu)), inv, zf) |
+                              (code_zp_f(half_bits_to_float((uint16_t)(p2 >> 16)), inv, zf) << 4));
+        }
+    }
+}
+
+hipError_t launch_quantize_zp(const void *w, int64_t n, int64_t k, void *packed, void *scales,
+                              void *zeros, hipStream_t stream)
+{
+    hipLaunchKernelGGL(quantize_rows_zp, dim3((unsigned)n), dim3(kQThreads), 0, stream,
+                       static_cast<const uint16_t *>(w), k, static_cast<uint8_t *>(packed),
+                       static_cast<uint16_t *>(scales), static_cast<uint8_t *>(zeros));
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void *w, int64_t n, int64_t k, void *packed, void *scales,
                            hipStream_t stream)
 {
