@@ -376,6 +376,7 @@ def extra_workloads(torch, w4, synth, dev, a):
     del ups, attn
 
     res["w8a16"] = int8_workloads(torch, w4, synth, dev, g)
+    res["w4a16_zp"] = zp_workloads(torch, w4, synth, dev, g)
 
     # quantizer: QKV-shaped fp16 weight -> packed + scales
     log("quantizer")
@@ -398,6 +399,82 @@ def extra_workloads(torch, w4, synth, dev, a):
         res["w8a16"]["full_decode_step_m8"] = full_step(torch, w4, synth, dev, synth.LAYER_LINEARS,
                                                         "INT8 70-layer decode step", cb=8)
     return res
+
+
+def linear_bytes_zp(m, n_rows, k, n_out):
+    """Algorithmic bytes of one zero-point INT4 linear call: packed codes,
+    fp16 scales, uint8 zero points, activations in, outputs out."""
+    return linear_bytes(m, n_rows, k, n_out) + n_rows
+
+
+def zp_workloads(torch, w4, synth, dev, g):
+    """The zero-point INT4 variant at the GLM-130B shapes: QKV decode per M,
+    the fused GeGLU up-projection at M = 1 and 16, and attention-out prefill
+    at M = 2048, all prepacked."""
+    log("zero-point INT4 workloads")
+    H, F, N = synth.HIDDEN, synth.FFN, synth.QKV_OUT
+
+    def rotating(n, k, dist, count, seed0):
+        out = []
+        for i in range(count):
+            w = synth.weight(n, k, synth.generator(seed0 + i, dev), dist, dev)
+            q, s, z = w4.quantize_rowwise_int4_zp(w)
+            del w
+            out.append((w4.w4a16_prepack(q), s, z))
+            del q
+        torch.cuda.synchronize()
+        return out
+
+    r = {}
+    qkv = rotating(N, H, "normal", 5, 900)
+    per_m = {}
+    for m in DECODE_MS:
+        x = synth.activations(m, H, g, dev)
+        y = torch.empty(m, N, dtype=torch.float16, device=dev)
+        c = [0]
+
+        def one(c=c, x=x, y=y):
+            qp, s, z = qkv[c[0] % len(qkv)]
+            c[0] += 1
+            w4.w4a16_zp_linear_prepacked(x, qp, s, z, y_out=y)
+
+        t = time_launches(torch, one, 30)
+        b = linear_bytes_zp(m, N, H, N)
+        per_m[str(m)] = {"us": round(t * 1e6, 2), "bytes": b, "GBs": round(b / t / 1e9, 1),
+                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+    r["decode_qkv_per_m"] = per_m
+    log(f"zero-point QKV decode: {per_m}")
+    del qkv
+    ups = rotating(2 * F, H, "t4", 3, 950)
+    gd = {}
+    for m in (1, 16):
+        xu = synth.activations(m, H, g, dev)
+        yu = torch.empty(m, F, dtype=torch.float16, device=dev)
+        c = [0]
+
+        def up(c=c, xu=xu, yu=yu):
+            qp, s, z = ups[c[0] % len(ups)]
+            c[0] += 1
+            w4.w4a16_zp_geglu_linear_prepacked(xu, qp, s, z, y_out=yu)
+
+        t = time_launches(torch, up, 20)
+        b = linear_bytes_zp(m, 2 * F, H, F)
+        gd[str(m)] = {"up_geglu_us": round(t * 1e6, 2), "up_geglu_GBs": round(b / t / 1e9, 1)}
+    r["decode_geglu_up"] = gd
+    del ups
+    attn = rotating(H, H, "normal", 1, 990)
+    M = synth.SEQ
+    x = synth.activations(M, H, g, dev)
+    y = torch.empty(M, H, dtype=torch.float16, device=dev)
+    t = time_launches(torch, lambda: w4.w4a16_zp_linear_prepacked(x, attn[0][0], attn[0][1], attn[0][2],
+                                                                    y_out=y), 10)
+    fl = 2.0 * M * H * H
+    r["prefill_m2048_attn_out"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                                   "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+    log(f"zero-point GeGLU and prefill: {gd} {r['prefill_m2048_attn_out']}")
+    del attn, x, y
+    torch.cuda.empty_cache()
+    return r
 
 
 def int8_workloads(torch, w4, synth, dev, g):

@@ -65,3 +65,8 @@ def test_int8_bytes_count_one_byte_per_code():
     n, k, m = 36864, 12288, 1
     assert bench.linear_bytes8(m, n, k, n) == n * k + 2 * n + 2 * m * k + 2 * m * n == 453_156_864
     assert bench.linear_bytes8(m, n, k, n) - bench.linear_bytes(m, n, k, n) == n * k // 2
+
+
+def test_zero_point_bytes_add_one_byte_per_row():
+    n, k, m = 36864, 12288, 8
+    assert bench.linear_bytes_zp(m, n, k, n) == bench.linear_bytes(m, n, k, n) + n
