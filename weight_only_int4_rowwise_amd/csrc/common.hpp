@@ -105,6 +105,14 @@ struct ZBias {
     half2v rm;   // (1024 + z, 64 + z): row-major order
 };
 
+// (w & m) ^ c as one v_bitop3_b32 (truth table 0x6a, index = 4 w + 2 m + c).
+// With c disjoint from m the compiler rewrites the plain expression as an
+// or, which it then emits as an and plus an or.
+__device__ __forceinline__ uint32_t and_xor(uint32_t w, uint32_t m, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(w, m, c, 0x6a);
+}
+
 __device__ __forceinline__ ZBias make_zbias(uint32_t z)
 {
     const _Float16 a = (_Float16)(1024.0f + (float)z), b = (_Float16)(64.0f + (float)z);
@@ -115,10 +123,10 @@ __device__ __forceinline__ half8 dequant8_zp(uint32_t packed, const ZBias &zb)
 {
     const uint32_t w8 = packed >> 8;
     u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, bits_to_h2((packed & 0x000F000Fu) | 0x64006400u) - zb.lo);
-    r[1] = __builtin_bit_cast(uint32_t, bits_to_h2((packed & 0x00F000F0u) | 0x54005400u) - zb.hi);
-    r[2] = __builtin_bit_cast(uint32_t, bits_to_h2((w8 & 0x000F000Fu) | 0x64006400u) - zb.lo);
-    r[3] = __builtin_bit_cast(uint32_t, bits_to_h2((w8 & 0x00F000F0u) | 0x54005400u) - zb.hi);
+    r[0] = __builtin_bit_cast(uint32_t, bits_to_h2(and_xor(packed, 0x000F000Fu, 0x64006400u)) - zb.lo);
+    r[1] = __builtin_bit_cast(uint32_t, bits_to_h2(and_xor(packed, 0x00F000F0u, 0x54005400u)) - zb.hi);
+    r[2] = __builtin_bit_cast(uint32_t, bits_to_h2(and_xor(w8, 0x000F000Fu, 0x64006400u)) - zb.lo);
+    r[3] = __builtin_bit_cast(uint32_t, bits_to_h2(and_xor(w8, 0x00F000F0u, 0x54005400u)) - zb.hi);
     return __builtin_bit_cast(half8, r);
 }
 
@@ -129,7 +137,7 @@ __device__ __forceinline__ half8 dequant8_rm_zp(uint32_t packed, const ZBias &zb
     for (int i = 0; i < 4; ++i) {
         const uint32_t sel = 0x0c000c00u | (uint32_t)i | ((uint32_t)i << 16);
         const uint32_t b = __builtin_amdgcn_perm(0u, packed, sel);
-        r[i] = __builtin_bit_cast(uint32_t, bits_to_h2((b & 0x00F0000Fu) | 0x54006400u) - zb.rm);
+        r[i] = __builtin_bit_cast(uint32_t, bits_to_h2(and_xor(b, 0x00F0000Fu, 0x54006400u)) - zb.rm);
     }
     return __builtin_bit_cast(half8, r);
 }
