@@ -253,7 +253,7 @@ def test_int8_two_decode_launches(m):
                                    (520, 2000, 256), (2000, 12280, 160)])
 def test_int8_prefill_shapes(m, n, k):
     """The MFMA GEMM path (m > 128) over INT8 codes: ragged m, n, k, small
-    and large grids, both layouts."""
+    grids (192 x 64 tiles) and large ones (192 x 128), both layouts."""
     g = synth.generator(2500 + m + n)
     w = synth.weight(n, k, g, "t4")
     bias = synth.normal_fp16((n,), 0.5, g)
@@ -263,7 +263,7 @@ def test_int8_prefill_shapes(m, n, k):
                  prepacked=qp)
 
 
-@pytest.mark.parametrize("m,f,k", [(129, 96, 256), (300, 512, 1056), (1000, 4080, 160)])
+@pytest.mark.parametrize("m,f,k", [(129, 96, 256), (300, 512, 1056), (1000, 4080, 160), (2000, 8192, 160)])
 def test_int8_prefill_geglu(m, f, k):
     g = synth.generator(2600 + m + f)
     w = synth.weight(2 * f, k, g, "t4")

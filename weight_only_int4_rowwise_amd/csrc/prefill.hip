@@ -332,17 +332,30 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //  * larger plain grids keep 128-token tiles unless they would fill the
     //    last wave of workgroups much worse than 64-token tiles (k <= 16384);
     //  * larger GeGLU grids take 128-token tiles.
-    //  * INT8 codes take 64-token tiles where INT4 takes 128: the second
-    //    weight register set per row group would not fit beside 128 tokens.
-    constexpr int WT = CB == 8 ? 4 : 8;
+    //  * INT8 codes need a second weight register set per row group, so
+    //    their large tiles keep 128 tokens with one row group fewer per
+    //    wave: 192 rows (GeGLU: 64 outputs) x 128 tokens, 188-204 VGPRs
+    //    and no spill, where 256 x 128 would spill.  Against 256 x 64
+    //    tiles at m = 2048: attention-out 498 against 559 us, plain FFN-up
+    //    2698 against 3046 us, GeGLU FFN-up 2929 against 3060 us.
     constexpr int out_per = 4 * 16 * (GEGLU ? 2 : 4);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
     const int64_t cus = compute_units();
     const int64_t g48 = tiles_n * ((m + 127) / 128);
-    if constexpr (GEGLU) {
+    if constexpr (CB == 8) {
+        if constexpr (GEGLU) {
+            if (g48 <= cus)
+                return launch_prefill_t<2, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+            return launch_prefill_t<2, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        } else {
+            if (4 * g48 <= 9 * cus && wave_fill(g48, 2 * cus) < 0.9)
+                return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+            return launch_prefill_t<3, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        }
+    } else if constexpr (GEGLU) {
         if (g48 <= cus)
             return launch_prefill_t<2, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
-        return launch_prefill_t<4, WT, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        return launch_prefill_t<4, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     } else {
         const int64_t slots = 2 * cus;
         const double fill8 = wave_fill(g48, slots);
@@ -351,7 +364,7 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
         if (k <= 16384 && fill4 > fill8 + 0.1)
             return launch_prefill_t<4, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
-        return launch_prefill_t<4, WT, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        return launch_prefill_t<4, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     }
 }
 
