@@ -147,7 +147,9 @@ w4a16_status w4a16_geglu_linear(const void *x_fp16, int64_t m, int64_t k,
  * w4a16_prepacked_bytes: size of the prepacked buffer,
  *   ceil(n/16) * ceil(k/128) * 1024, or -1 if n < 0, k <= 0 or k % 32 != 0.
  * w4a16_prepack: q_packed [n][k/2] (device) -> q_prepacked (device,
- *   w4a16_prepacked_bytes(n, k) bytes).  k % 32 == 0.
+ *   w4a16_prepacked_bytes(n, k) bytes).  k % 32 == 0.  The reorder moves
+ *   nibbles without reading them, so it serves the unsigned codes of the
+ *   zero-point variant (w4a16_zp.h) as well.
  * w4a16_linear_prepacked / w4a16_geglu_linear_prepacked: exactly
  *   w4a16_linear / w4a16_geglu_linear with the weight in the prepacked
  *   layout; the GeGLU form needs f % 16 == 0 (the gate / value boundary
