@@ -387,7 +387,24 @@ def extra_workloads(torch, w4, synth, dev, a):
     qb = synth.QKV_OUT * H * 2 + synth.QKV_OUT * H // 2 + 2 * synth.QKV_OUT
     res["quantize_qkv"] = {"us": round(t * 1e6, 1), "GBs": round(qb / t / 1e9, 1),
                            "frac_hbm": round(qb / t / 1e9 / HBM_PEAK_GBS, 4)}
-    del wq, qo, so
+    del qo
+    # the variants' quantizers on the same weight: INT8 codes (one byte per
+    # code) and the zero-point codes (packed codes, scales, zero points)
+    co = torch.empty(synth.QKV_OUT, H, dtype=torch.int8, device=dev)
+    t = time_launches(torch, lambda: w4.quantize_rowwise_int8(wq, q_out=co, s_out=so), 10)
+    qb8 = synth.QKV_OUT * H * 2 + synth.QKV_OUT * H + 2 * synth.QKV_OUT
+    res["quantize_qkv_int8"] = {"us": round(t * 1e6, 1), "GBs": round(qb8 / t / 1e9, 1),
+                                "frac_hbm": round(qb8 / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del co
+    qo = torch.empty(synth.QKV_OUT, H // 2, dtype=torch.uint8, device=dev)
+    zo = torch.empty(synth.QKV_OUT, dtype=torch.uint8, device=dev)
+    t = time_launches(torch, lambda: w4.quantize_rowwise_int4_zp(wq, q_out=qo, s_out=so, z_out=zo), 10)
+    qbz = qb + synth.QKV_OUT
+    res["quantize_qkv_zero_point"] = {"us": round(t * 1e6, 1), "GBs": round(qbz / t / 1e9, 1),
+                                      "frac_hbm": round(qbz / t / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"quantizers: {res['quantize_qkv']} int8 {res['quantize_qkv_int8']} "
+        f"zero-point {res['quantize_qkv_zero_point']}")
+    del wq, qo, so, zo
 
     if not a.no_full_step:
         res["full_decode_step_m8"] = full_step(torch, w4, synth, dev, synth.LAYER_LINEARS,

@@ -382,12 +382,119 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_zp(const uint16_t *__
     }
 }
 
+// Register-resident zero-point path (k % 8 == 0, rows up to 512 WPR CH
+// halves): the layout of quantize_rows_reg, with the row's min and max
+// reduced instead of its absmax, so HBM is read once.
+template <int WPR, int CH>
+__global__ __launch_bounds__(kQThreads) void quantize_rows_zp_reg(const uint16_t *__restrict__ w,
+                                                                  int64_t n, int64_t k,
+                                                                  uint8_t *__restrict__ packed,
+                                                                  uint16_t *__restrict__ scales,
+                                                                  uint8_t *__restrict__ zeros)
+{
+    constexpr int RPW = (kQThreads / kWave) / WPR;          // rows per workgroup
+    __shared__ float red[2][kQThreads / kWave];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int part = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const bool live = row < n;
+    const int64_t rowc = live ? row : n - 1;
+    const int64_t nchunk = k / 8;
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(w + rowc * k, k * 2);
+
+    u32x4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+        v[c] = buf_load16_stream(rs_w, idx < nchunk ? (uint32_t)(idx * 16) : kOutOfRange);
+    }
+    // chunks past the row read zeros, which min(., 0) and max(., 0) absorb
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = half_bits_to_float((uint16_t)(v[c][j] & 0xFFFFu));
+            const float b = half_bits_to_float((uint16_t)(v[c][j] >> 16));
+            lo = fminf(lo, fminf(a, b));
+            hi = fmaxf(hi, fmaxf(a, b));
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+    }
+    if (WPR > 1) {
+        if (lane == 0) {
+            red[0][wave] = lo;
+            red[1][wave] = hi;
+        }
+        __syncthreads();
+        const int w0 = wave - part;
+#pragma unroll
+        for (int p = 0; p < WPR; ++p) {
+            lo = fminf(lo, red[0][w0 + p]);
+            hi = fmaxf(hi, red[1][w0 + p]);
+        }
+    }
+    const uint16_t sb = float_to_half_bits((float)(((double)hi - (double)lo) / 15.0));
+    const float sf = half_bits_to_float(sb);
+    float inv = 0.0f, zf = 0.0f;
+    if (sf != 0.0f) {
+        inv = __fdiv_rn(1.0f, sf);
+        zf = __builtin_amdgcn_fmed3f((float)__builtin_rint(-(double)lo / (double)sf), 0.0f, 15.0f);
+    }
+    if (live && part == 0 && lane == 0) {
+        scales[row] = sb;
+        zeros[row] = (uint8_t)zf;
+    }
+    if (!live)
+        return;
+    uint32_t *pr = reinterpret_cast<uint32_t *>(packed + row * (k / 2));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int64_t idx = ((int64_t)c * WPR + part) * kWave + lane;
+        if (idx < nchunk) {
+            uint32_t out = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out |= code_zp_f(half_bits_to_float((uint16_t)(v[c][j] & 0xFFFFu)), inv, zf) << (8 * j);
+                out |= code_zp_f(half_bits_to_float((uint16_t)(v[c][j] >> 16)), inv, zf) << (8 * j + 4);
+            }
+            pr[idx] = out;
+        }
+    }
+}
+
 hipError_t launch_quantize_zp(const void *w, int64_t n, int64_t k, void *packed, void *scales,
                               void *zeros, hipStream_t stream)
 {
-    hipLaunchKernelGGL(quantize_rows_zp, dim3((unsigned)n), dim3(kQThreads), 0, stream,
-                       static_cast<const uint16_t *>(w), k, static_cast<uint8_t *>(packed),
-                       static_cast<uint16_t *>(scales), static_cast<uint8_t *>(zeros));
+    const uint16_t *wp = static_cast<const uint16_t *>(w);
+    uint8_t *pp = static_cast<uint8_t *>(packed);
+    uint16_t *sp = static_cast<uint16_t *>(scales);
+    uint8_t *zp = static_cast<uint8_t *>(zeros);
+    const int64_t lane_chunks = (k / 8 + kWave - 1) / kWave;
+#define ZP_QREG(WPR, CH)                                                                           \
+    hipLaunchKernelGGL((quantize_rows_zp_reg<WPR, CH>),                                            \
+                       dim3((unsigned)((n + (4 / WPR) - 1) / (4 / WPR))), dim3(kQThreads), 0,       \
+                       stream, wp, n, k, pp, sp, zp)
+    if (k % 8 == 0 && lane_chunks <= 64) {
+        if (lane_chunks <= 4)
+            ZP_QREG(1, 4);
+        else if (lane_chunks <= 8)
+            ZP_QREG(1, 8);
+        else if (lane_chunks <= 16)
+            ZP_QREG(1, 16);
+        else if (lane_chunks <= 32)
+            ZP_QREG(2, 16);
+        else
+            ZP_QREG(4, 16);
+    } else {
+        hipLaunchKernelGGL(quantize_rows_zp, dim3((unsigned)n), dim3(kQThreads), 0, stream, wp, k, pp,
+                           sp, zp);
+    }
+#undef ZP_QREG
     return hipGetLastError();
 }
 
