@@ -563,56 +563,84 @@ def int8_workloads(torch, w4, synth, dev, g):
     return r
 
 
-def full_step(torch, w4, synth, dev, linears, label, cb=4):
-    """70 layers x the four linears of `linears` (name, rows, k) at M = 8,
-    all weights resident and prepacked (INT4, or INT8 for cb = 8), launched
-    back to back on one stream."""
-    log(f"{label}: generating and quantizing {synth.LAYERS * len(linears)} matrices")
-    layers = []
-    for l in range(synth.LAYERS):
-        mats = []
-        for mid, (name, n, k) in enumerate(linears):
-            g = synth.generator(synth.layer_weight_seed(l, mid), dev)
-            w = synth.weight(n, k, g, device=dev)
-            if cb == 8:
-                q, s = w4.quantize_rowwise_int8(w)
-                del w
-                mats.append((w4.w8a16_prepack(q), s))
-            else:
-                q, s = w4.quantize_rowwise_int4(w)
-                del w
-                mats.append((w4.w4a16_prepack(q), s))
-            del q
-        layers.append(mats)
-    torch.cuda.synchronize()
-    g = synth.generator(7, dev)
+class FullStep:
+    """The full-model decode step: 70 layers x the four linears of `linears`
+    (name, rows, k) at M = 8, every weight drawn on the GPU with seed
+    1000 layer + matrix id, quantized (INT4, or INT8 for cb = 8), prepacked
+    and kept resident; one fixed N(0, 1) input of each width (generator 7);
+    the 280 launches back to back on one stream.
+
+    keep: layers whose inputs are also copied to the host for a parity
+    check: kept[layer] = [(fp16 weight bits, row-major codes, scale bits)]
+    per linear, in `linears` order."""
+
     M = 8
-    xs = {k: synth.activations(M, k, g, dev) for k in sorted({k for _, _, k in linears})}
-    calls = []
-    total = 0
-    for name, n, k in linears:
-        geglu = name == "ffn_up"
-        out = n // 2 if geglu else n
-        if cb == 8:
-            fn = w4.w8a16_geglu_linear_prepacked if geglu else w4.w8a16_linear_prepacked
-            total += linear_bytes8(M, n, k, out)
-        else:
-            fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
-            total += linear_bytes(M, n, k, out)
-        calls.append((fn, xs[k], torch.empty(M, out, dtype=torch.float16, device=dev)))
-    total *= synth.LAYERS
 
-    def run():
-        for mats in layers:
-            for (fn, x, y), (qp, s) in zip(calls, mats):
+    def __init__(self, torch, w4, synth, dev, linears, cb=4, keep=(), label="decode step"):
+        import numpy as np
+        log(f"{label}: generating and quantizing {synth.LAYERS * len(linears)} matrices")
+        self.linears = tuple(linears)
+        self.layers, self.kept = [], {}
+
+        def host_bits(t):
+            return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+        for l in range(synth.LAYERS):
+            mats = []
+            for mid, (name, n, k) in enumerate(self.linears):
+                g = synth.generator(synth.layer_weight_seed(l, mid), dev)
+                w = synth.weight(n, k, g, device=dev)
+                if cb == 8:
+                    q, s = w4.quantize_rowwise_int8(w)
+                    qp = w4.w8a16_prepack(q)
+                else:
+                    q, s = w4.quantize_rowwise_int4(w)
+                    qp = w4.w4a16_prepack(q)
+                if l in keep:
+                    self.kept.setdefault(l, []).append((host_bits(w), q.cpu().numpy(), host_bits(s)))
+                del w, q
+                mats.append((qp, s))
+            self.layers.append(mats)
+            if l % 10 == 9:
+                log(f"{label}: {l + 1} layers resident")
+        torch.cuda.synchronize()
+        g = synth.generator(7, dev)
+        widths = sorted({k for _, _, k in self.linears})
+        self.x = {k: synth.activations(self.M, k, g, dev) for k in widths}
+        self.calls = []
+        total = 0
+        for name, n, k in self.linears:
+            geglu = name == "ffn_up"
+            out = n // 2 if geglu else n
+            if cb == 8:
+                fn = w4.w8a16_geglu_linear_prepacked if geglu else w4.w8a16_linear_prepacked
+                total += linear_bytes8(self.M, n, k, out)
+            else:
+                fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+                total += linear_bytes(self.M, n, k, out)
+            self.calls.append((fn, self.x[k], torch.empty(self.M, out, dtype=torch.float16, device=dev)))
+        self.bytes = total * synth.LAYERS
+
+    def run(self, after_layer=None):
+        """One step; after_layer(l), if given, runs after layer l's launches
+        are queued (outputs y of self.calls then hold layer l's results once
+        the stream reaches that point)."""
+        for l, mats in enumerate(self.layers):
+            for (fn, x, y), (qp, s) in zip(self.calls, mats):
                 fn(x, qp, s, y_out=y)
+            if after_layer is not None:
+                after_layer(l)
 
-    t = time_launches(torch, run, 3, warm=1)
-    r = {"ms": round(t * 1e3, 3), "bytes": total, "GBs": round(total / t / 1e9, 1),
-         "frac_hbm": round(total / t / 1e9 / HBM_PEAK_GBS, 4),
+
+def full_step(torch, w4, synth, dev, linears, label, cb=4):
+    """Times FullStep: 70 layers x 4 linears at M = 8."""
+    step = FullStep(torch, w4, synth, dev, linears, cb=cb, label=label)
+    t = time_launches(torch, step.run, 3, warm=1)
+    r = {"ms": round(t * 1e3, 3), "bytes": step.bytes, "GBs": round(step.bytes / t / 1e9, 1),
+         "frac_hbm": round(step.bytes / t / 1e9 / HBM_PEAK_GBS, 4),
          "shapes": [[name, n, k] for name, n, k in linears]}
     log(f"{label}: {r}")
-    del layers
+    del step
     torch.cuda.empty_cache()
     return r
 

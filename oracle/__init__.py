@@ -44,7 +44,9 @@ class OracleError(RuntimeError):
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (no HIP, no shared code with the GPU path)."""
-    if force or not os.path.exists(_LIB_PATH):
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
                "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
@@ -60,8 +62,7 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        build(force=False)                 # compiles only if missing or older than the source
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int64
@@ -71,6 +72,7 @@ def _load():
         lib.oracle_double_to_half.restype = ctypes.c_uint16
         lib.oracle_gelu.argtypes = [ctypes.c_double]
         lib.oracle_gelu.restype = ctypes.c_double
+        lib.oracle_gelu_n.argtypes = [P, I, P]
         lib.oracle_quantize_codes.argtypes = [P, I, I, P, P]
         lib.oracle_quantize_rowwise_int4.argtypes = [P, I, I, P, P]
         lib.oracle_unpack_int4.argtypes = [P, I, I, P]
@@ -134,6 +136,14 @@ def double_to_half(values) -> np.ndarray:
 
 def gelu(t: float) -> float:
     return float(_load().oracle_gelu(float(t)))
+
+
+def gelu_n(t) -> np.ndarray:
+    """GELU of every entry of a float64 array (same shape)."""
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    out = np.empty_like(t)
+    _load().oracle_gelu_n(_ptr(t), t.size, _ptr(out))
+    return out
 
 
 def quantize_codes(w):
@@ -401,12 +411,14 @@ def geglu_bound(g_ref, a_ref, b_ref, mag_a, mag_b):
     """Bound for g = GELU(a)*b computed from a and b that each carry at most
     their linear bound eps_a, eps_b of error.
 
-    By the mean value theorem |GELU(a') - GELU(a)| <= 1.13 * eps_a, since
-    |GELU'| = |Phi(t) + t*phi(t)| <= 1.13 on the real line; |GELU(a)| <= |a|
-    since 0 <= Phi <= 1.  So |g' - g| <= 1.13|b|eps_a + |a|eps_b
-    + 1.13 eps_a eps_b, plus the final fp16 rounding (2^-11 relative, taken
-    as 2^-10 to cover fp32 evaluation of GELU itself) and the 1e-4 floor."""
+    With a' = a + da, b' = b + db (|da| <= eps_a, |db| <= eps_b):
+    GELU(a')b' - GELU(a)b = (GELU(a') - GELU(a))b' + GELU(a)(b' - b), and by
+    the mean value theorem |GELU(a') - GELU(a)| <= 1.13 eps_a, since
+    |GELU'| = |Phi(t) + t phi(t)| <= 1.13 on the real line.  So
+    |g' - g| <= 1.13|b|eps_a + |GELU(a)|eps_b + 1.13 eps_a eps_b, plus the
+    final fp16 rounding (2^-11 relative, taken as 2^-10 to cover fp32
+    evaluation of GELU itself) and the 1e-4 floor."""
     ea = linear_bound(mag_a)
     eb = linear_bound(mag_b)
-    return (1.13 * np.abs(b_ref) * ea + np.abs(a_ref) * eb + 1.13 * ea * eb
+    return (1.13 * np.abs(b_ref) * ea + np.abs(gelu_n(a_ref)) * eb + 1.13 * ea * eb
             + 2.0 ** -10 * np.abs(g_ref) + LINEAR_ABS)

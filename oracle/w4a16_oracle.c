@@ -306,6 +306,13 @@ double oracle_gelu(double t)
     return 0.5 * t * (1.0 + erf(t / sqrt(2.0)));
 }
 
+/* out[i] = GELU(t[i]) for i < n. */
+void oracle_gelu_n(const double *t, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_gelu(t[i]);
+}
+
 /* g[i][j] = GELU(a[i][j]) * b[i][j], where a is the linear through weight
  * rows [0, f) and b the linear through rows [f, 2f) of the up-projection.
  * Reading: the first half of the rows is the GELU-gated one.  a, b and their

@@ -102,6 +102,46 @@ def test_binding_refuses_cpu_tensors():
         w4.quantize_rowwise_int4(w)
 
 
+class _OnGpu:
+    """Stand-in for a GPU tensor of a given shape on GPU `index`: only what the
+    binding reads before its device checks (never launched)."""
+
+    def __init__(self, shape, index):
+        self.shape = tuple(shape)
+        self.device = f"cuda:{index}"
+        self._index = index
+
+    def dim(self):
+        return len(self.shape)
+
+    def get_device(self):
+        return self._index
+
+
+@pytest.mark.parametrize("which", ["int4", "int8", "zp"])
+def test_quantizers_refuse_outputs_on_another_gpu(monkeypatch, which):
+    """Every quantizer checks that caller-supplied outputs sit on w's GPU
+    before it launches (the dtype and layout checks are bypassed here, since
+    there is no GPU tensor without a GPU)."""
+    import weight_only_int4_rowwise_amd as w4
+    monkeypatch.setattr(w4, "_require", lambda *a, **kw: None)
+    n, k = 4, 32
+    w = _OnGpu((n, k), 0)
+    cols = k // 2 if which != "int8" else k
+    good_q, bad_q = _OnGpu((n, cols), 0), _OnGpu((n, cols), 1)
+    good_s, bad_s = _OnGpu((n,), 0), _OnGpu((n,), 1)
+    if which == "int4":
+        fn = lambda q, s: w4.quantize_rowwise_int4(w, q_out=q, s_out=s)
+    elif which == "int8":
+        fn = lambda q, s: w4.quantize_rowwise_int8(w, q_out=q, s_out=s)
+    else:
+        fn = lambda q, s: w4.quantize_rowwise_int4_zp(w, q_out=q, s_out=s, z_out=_OnGpu((n,), 0))
+    with pytest.raises(ValueError, match="q_out on cuda:1"):
+        fn(bad_q, good_s)
+    with pytest.raises(ValueError, match="s_out on cuda:1"):
+        fn(good_q, bad_s)
+
+
 def test_prepacked_size_and_checks(lib):
     assert lib.w4a16_prepacked_bytes(16, 128) == 1024
     assert lib.w4a16_prepacked_bytes(17, 128) == 2048

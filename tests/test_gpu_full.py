@@ -5,7 +5,9 @@ Inputs are drawn on the GPU (seeded ``torch.Generator('cuda')``; the same
 tensors are copied to the host for the oracle).  Quantized bytes and scales
 are compared in full; decode outputs (m <= 64) in full; two-launch decode
 (m = 100) and prefill outputs (m = 512, 2048) on sampled rows and columns
-that touch every output tile.
+that touch every output tile.  The 70-layer decode step runs as the
+benchmark builds and launches it, and its first and last layers are
+checked in full.
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ import oracle
 import weight_only_int4_rowwise_amd as w4
 from weight_only_int4_rowwise_amd import synth
 
+import bench
 from helpers import announce, assert_bits_equal, assert_within, bits, f64, u8
 
 pytestmark = pytest.mark.gpu
@@ -121,8 +124,8 @@ _SHARDS = {"qkv/4": (9216, 12288, False, "normal"), "attn_out/4": (12288, 3072, 
 
 @pytest.mark.parametrize("name", list(_SHARDS))
 def test_tensor_parallel_shard_decode(name):
-    """Decode on one GPU's shard at m = 1, 8, 32, 48 (prepacked weights),
-    every output against the oracle."""
+    """Decode on one GPU's shard at every token class, m = 1, 8, 16, 32, 48,
+    64 (prepacked weights), every output against the oracle."""
     n, k, geglu, dist = _SHARDS[name]
     rows = 2 * n if geglu else n
     g = synth.generator(3100 + rows + k, DEV)
@@ -130,7 +133,7 @@ def test_tensor_parallel_shard_decode(name):
     q, s, p_ref, s_ref = _quantize_checked(w, f"shard {name} {rows}x{k}")
     del w
     qp = w4.w4a16_prepack(q)
-    for m in (1, 8, 32, 48):
+    for m in (1, 8, 16, 32, 48, 64):
         x = synth.activations(m, k, g, DEV)
         announce("shard decode", name, m)
         if geglu:
@@ -260,3 +263,50 @@ def test_largest_accepted_weight():
     torch.cuda.synchronize()
     r = assert_within(_gather(y, mi, ni), gr, oracle.geglu_bound(gr, a, b, ma, mb), "largest GeGLU m=8")
     print(f"largest GeGLU m=8: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
+# ------------------------------------------------- 70-layer decode step
+
+@pytest.mark.timeout(900)
+def test_full_decode_step_70_layers():
+    """The full-model decode step as the benchmark runs it (GLM-130B paper
+    card, "Paper vs code": QKV, attention output and both MLP projections
+    quantized in every layer; "Hyperparameters": 70 layers): 280 matrices
+    drawn on the GPU with seeds 1000 layer + matrix id, quantized, prepacked
+    and resident (63.4 GB), M = 8 inputs from generator 7, all 280 launches
+    in one stream.  Layers 0 and 69: packed codes and scales bit-exact with
+    the oracle's quantization of the same fp16 weights, and every output of
+    QKV, attention-out, the fused GeGLU up-projection and down within the
+    bound."""
+    check = (0, synth.LAYERS - 1)
+    announce("70-layer step: building", synth.LAYER_LINEARS)
+    step = bench.FullStep(torch, w4, synth, DEV, synth.LAYER_LINEARS, keep=check,
+                          label="70-layer step parity")
+    snaps = {}
+
+    def snap(layer):
+        if layer in check:
+            snaps[layer] = [y.clone() for _, _, y in step.calls]
+
+    announce("70-layer step: 280 launches", step.bytes)
+    step.run(after_layer=snap)
+    torch.cuda.synchronize()
+    for layer in check:
+        for (name, n, k), (_, x, _), (w_bits, q_gpu, s_gpu), y in zip(
+                step.linears, step.calls, step.kept[layer], snaps[layer]):
+            what = f"layer {layer} {name} {n}x{k}"
+            announce("70-layer step: oracle", what)
+            p_ref, s_ref = oracle.quantize_rowwise_int4(w_bits)
+            del w_bits
+            assert_bits_equal(s_gpu, s_ref, f"{what}: scales")
+            assert_bits_equal(q_gpu, p_ref, f"{what}: packed")
+            if name == "ffn_up":
+                g, a, b, ma, mb = oracle.geglu(bits(x), p_ref, s_ref)
+                r = assert_within(f64(y), g, oracle.geglu_bound(g, a, b, ma, mb), what)
+            else:
+                y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
+                r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), what)
+            print(f"{what}: {y.numel()} outputs, max err/bound {r:.4f}", flush=True)
+        step.kept[layer] = None
+    del step, snaps
+    torch.cuda.empty_cache()

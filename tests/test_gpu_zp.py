@@ -120,6 +120,18 @@ def test_zp_quantize_symmetric_enumeration():
         quantize_both(synth.enumeration_rows(a, k), f"zp enumeration rows {start}.. k={k}")
 
 
+@pytest.mark.parametrize("k", [8, 10])
+def test_zp_quantize_asymmetric_ranges(k):
+    """Scales of asymmetric ranges must be one rounding of (hi - lo) / 15:
+    rows [1934, -0.0624694824, 0 ...] and [1.888671875, -6.0976e-05, 0 ...]
+    and 1.6 M more range pairs (k = 8: the register-resident kernel, k = 10:
+    the two-sweep kernel)."""
+    hi, lo = synth.asymmetric_range_pairs()
+    hi = torch.cat([torch.tensor([1934.0, 1.888671875], dtype=torch.float16), hi])
+    lo = torch.cat([torch.tensor([-0.062469482421875, -6.0976e-05], dtype=torch.float16), lo])
+    quantize_both(synth.range_end_rows(hi, lo, k), f"asymmetric range ends k={k}")
+
+
 def test_zp_quantize_zero_and_tiny_rows():
     w = torch.zeros(4, 64, dtype=torch.float16)
     w[1, 3] = torch.tensor(7, dtype=torch.int16).view(torch.float16)      # (hi - lo)/15 rounds to 0

@@ -580,3 +580,52 @@ def test_zp_linear_and_geglu_vs_numpy(oracle_mod):
     a = x.astype(np.float64) @ wh[:f].T
     b = x.astype(np.float64) @ wh[f:].T
     assert np.allclose(gg, a * norm.cdf(a) * b, rtol=1e-11, atol=1e-13)
+
+
+def test_zp_scale_on_wide_asymmetric_ranges(oracle_mod):
+    """Ranges whose hi - lo needs up to 40 significant bits (the GPU test's
+    set of range pairs): the oracle's scale is the nearest fp16 to the exact
+    (hi - lo) / 15 on the two rows where rounding through fp32 goes wrong,
+    and on every row of the set where fp32-then-fp16 differs from one
+    rounding of the binary64 quotient; the set holds hundreds of such rows,
+    so a quantizer that rounds twice fails the GPU test."""
+    hi, lo = synth.asymmetric_range_pairs()
+    hi = hi.numpy().astype(np.float64)
+    lo = lo.numpy().astype(np.float64)
+    q = (hi - lo) / 15.0
+    twice = q.astype(np.float32).astype(np.float16).view(np.uint16)
+    trap = np.flatnonzero(twice != q.astype(np.float16).view(np.uint16))
+    once = np.array([_nearest_fp16_exact((Fraction(hi[i]) - Fraction(lo[i])) / 15) for i in trap],
+                    dtype=np.uint16)
+    rows = np.zeros((trap.size + 2, 2), dtype=np.float16)
+    rows[:trap.size, 0], rows[:trap.size, 1] = hi[trap], lo[trap]
+    rows[trap.size] = [1934.0, -0.062469482421875]
+    rows[trap.size + 1] = [1.888671875, -6.0976e-05]
+    _, s, _ = oracle_mod.quantize_codes_zp(rows)
+    # numpy's float64 -> float16 cast is itself one rounding; where it and the
+    # fp32 path disagree the exact rational decides
+    assert trap.size >= 500
+    assert np.array_equal(s[:trap.size], once)
+    assert np.all(once != twice[trap])
+    assert s[trap.size] == 0x5807            # 128.875, not 129
+    exact = (Fraction(1.888671875) - Fraction(float(np.float16(-6.0976e-05)))) / 15
+    assert s[trap.size + 1] == _nearest_fp16_exact(exact)
+
+
+def test_geglu_bound_scales_value_error_by_gelu_of_gate(oracle_mod):
+    """The value-half term of the GeGLU bound is |GELU(a)| eps_b, not
+    |a| eps_b: at a = -3 (Phi(-3) from the golden table) an error in b
+    passes through GELU(a) = -3 Phi(-3), 740 times smaller than |a|."""
+    with open(os.path.join(GOLDEN, "gelu_values.txt")) as fh:
+        phi = {float(t): float(p) for t, p in (l.split() for l in fh if l.strip() and not l.startswith("#"))}
+    a = np.array([-3.0, -1.0, 2.0])
+    b = np.array([1.5, -0.5, 0.25])
+    mag_a = np.array([0.0, 0.0, 0.0])       # eps_a = 1e-4 (the floor only)
+    mag_b = np.array([10.0, 10.0, 10.0])    # eps_b = 2e-3 * 10 + 1e-4
+    g = np.array([t * phi[t] for t in a]) * b
+    got = oracle_mod.geglu_bound(g, a, b, mag_a, mag_b)
+    ea, eb = 1e-4, 2e-3 * 10 + 1e-4
+    want = (1.13 * np.abs(b) * ea + np.abs([t * phi[t] for t in a]) * eb + 1.13 * ea * eb
+            + 2.0 ** -10 * np.abs(g) + 1e-4)
+    assert got == pytest.approx(want, rel=1e-12)
+    assert got[0] < 0.05 * abs(a[0]) * eb      # the |a| form would allow 20x more here

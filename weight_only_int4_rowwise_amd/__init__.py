@@ -146,7 +146,10 @@ def quantize_rowwise_int4(w, q_out=None, s_out=None):
     _require(s_out, torch.float16, "s_out")
     if tuple(q_out.shape) != (n, k // 2) or tuple(s_out.shape) != (n,):
         raise ValueError("output shape mismatch")
-    st = _launch(lib.quantize_rowwise_int4, w.get_device(),
+    dev = w.get_device()
+    _same_device(q_out, dev, "q_out", "quantize_rowwise_int4")
+    _same_device(s_out, dev, "s_out", "quantize_rowwise_int4")
+    st = _launch(lib.quantize_rowwise_int4, dev,
                  w.data_ptr(), n, k, q_out.data_ptr(), s_out.data_ptr())
     _lib.check(st, "quantize_rowwise_int4")
     return q_out, s_out

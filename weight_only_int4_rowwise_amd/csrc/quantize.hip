@@ -290,13 +290,41 @@ static hipError_t launch_quantize_q(const void *w, int64_t n, int64_t k, void *p
 //   s  = fp16((hi - lo) / 15),  z = clamp(round_half_even(-lo / s), 0, 15)
 //   q  = clamp(round_half_even(W / s) + z, 0, 15)   (unsigned nibbles)
 // One 256-thread workgroup per row, two sweeps (the second hits in cache).
-// Exactness: hi - lo is exact in binary64, the division is correctly
-// rounded, and rounding that to fp32 then fp16 is the correctly rounded fp16
-// quotient (53 -> 24 -> 11 bits: 24 >= 2 * 11 + 2).  -lo / s in binary64 is
+// Exactness: hi - lo is exact in binary64 (it can need up to 40 significant
+// bits) and the division is correctly rounded.  The binary64 quotient is
+// then rounded to fp16 once (half_bits_of_double): converting it to fp32
+// with ties to even and then to fp16 would round twice, and that is not
+// harmless here because the dividend has more than 11 significant bits
+// (row [1934, -0.0624694824, 0, ...]: the quotient 128.9374980 lands on the
+// fp32 value 128.9375, an fp16 tie, which then goes up to 129 instead of
+// down to 128.875).  The binary64 quotient itself is the correctly rounded
+// fp16 quotient's source: a non-midpoint quotient of a multiple of 2^-24 by
+// 15 lies at least 2^-24 / 15 from every fp16 midpoint, far more than a
+// binary64 rounding moves it.  -lo / s in binary64 is
 // far closer to the exact quotient than the 2^-12 gap that separates a
 // non-tie quotient from a half-integer, so rint gives its round-half-even.
 // The codes follow the INT4 steps (|w / s| <= 15 here).
 // ---------------------------------------------------------------------------
+// fp16 bits of a finite binary64 value, rounded once (to nearest, ties to
+// even).  The value goes to fp32 by round-to-odd (the nearest fp32, stepped
+// back towards zero if it rounded away, with its last bit set whenever the
+// conversion was inexact), which keeps enough of the dropped part for the
+// final fp32 -> fp16 rounding to be the correctly rounded one: 24 >= 11 + 2
+// bits.  fp16 results that are subnormal keep fewer bits, so the margin only
+// grows.
+__device__ __forceinline__ uint16_t half_bits_of_double(double d)
+{
+    const float f = (float)d;
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    const double back = (double)f;
+    if (back != d) {
+        if (__builtin_fabs(back) > __builtin_fabs(d))
+            b -= 1u;                    // sign-magnitude: one step towards zero
+        b |= 1u;
+    }
+    return float_to_half_bits(__builtin_bit_cast(float, b));
+}
+
 __device__ __forceinline__ uint32_t code_zp_f(float wf, float inv, float zf)
 {
     const float r = wf * inv;
@@ -352,7 +380,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_zp(const uint16_t *__
         lo = fminf(lo, red[0][i]);
         hi = fmaxf(hi, red[1][i]);
     }
-    const uint16_t sb = float_to_half_bits((float)(((double)hi - (double)lo) / 15.0));
+    const uint16_t sb = half_bits_of_double(((double)hi - (double)lo) / 15.0);
     const float s = half_bits_to_float(sb);
     float inv = 0.0f, zf = 0.0f;
     if (s != 0.0f) {
@@ -438,7 +466,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_zp_reg(const uint16_t
             hi = fmaxf(hi, red[1][w0 + p]);
         }
     }
-    const uint16_t sb = float_to_half_bits((float)(((double)hi - (double)lo) / 15.0));
+    const uint16_t sb = half_bits_of_double(((double)hi - (double)lo) / 15.0);
     const float sf = half_bits_to_float(sb);
     float inv = 0.0f, zf = 0.0f;
     if (sf != 0.0f) {

@@ -168,6 +168,34 @@ def exponent_rows(n: int, k: int, gen: torch.Generator, e_lo: int = -8, e_hi: in
     return vals.to(torch.float16)
 
 
+def range_end_rows(hi, lo, k: int) -> torch.Tensor:
+    """One row per pair (hi[i], lo[i]) of fp16 values: the row holds hi, then
+    lo, then zeros to k entries (k >= 2), so its range ends are exactly hi and
+    lo (and 0)."""
+    hi = torch.as_tensor(hi, dtype=torch.float16).reshape(-1)
+    lo = torch.as_tensor(lo, dtype=torch.float16).reshape(-1)
+    rows = torch.zeros(hi.numel(), k, dtype=torch.float16)
+    rows[:, 0] = hi
+    rows[:, 1] = lo
+    return rows
+
+
+def asymmetric_range_pairs():
+    """(hi, lo) pairs of range ends for rows [hi, lo, 0, ...]: every finite
+    positive fp16 hi against lo values with many significant bits (all-ones
+    subnormals -(2^j - 1) 2^-24, full-mantissa normals -2047 2^(e-10), and
+    -1365 2^-24), then the mirror images (hi, lo) -> (-lo, -hi).  hi - lo then
+    needs up to 40 significant bits, and (hi - lo) / 15 lands next to fp16
+    midpoints in ways a symmetric range never does."""
+    his = all_finite_nonneg_fp16()[1:].to(torch.float64)
+    los = ([-(2 ** j - 1) * 2.0 ** -24 for j in range(1, 12)]
+           + [-2047 * 2.0 ** (e - 10) for e in range(-14, 0)] + [-1365 * 2.0 ** -24])
+    hi = torch.cat([his] * len(los))
+    lo = torch.cat([torch.full_like(his, v) for v in los])
+    hi, lo = torch.cat([hi, -lo]), torch.cat([lo, -hi])
+    return hi.to(torch.float16), lo.to(torch.float16)
+
+
 def small_int_activations(m: int, k: int, gen: torch.Generator, lo: int = -3, hi: int = 3) -> torch.Tensor:
     """Integer-valued fp16 activations in [lo, hi]."""
     return torch.randint(lo, hi + 1, (m, k), generator=gen).to(torch.float16)
