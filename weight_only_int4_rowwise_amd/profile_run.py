@@ -1,35 +1,41 @@
-"""Fixed launch sequence for hardware-counter runs (rocprofv3 --pmc).
+"""Fixed launch sequences for profiler runs (rocprofv3 --pmc / --kernel-trace),
+and the summaries made from their output.
 
-    python -m weight_only_int4_rowwise_amd.profile_run --m 64 --reps 10
+    python -m weight_only_int4_rowwise_amd.profile_run decode --m 64 --reps 10
+    python -m weight_only_int4_rowwise_amd.profile_run prefill --reps 5
+    python -m weight_only_int4_rowwise_amd.profile_run step --reps 20
+    python -m weight_only_int4_rowwise_amd.profile_run summarize-pmc DIR...
+    python -m weight_only_int4_rowwise_amd.profile_run summarize-trace DIR
 
-Launches the decode QKV linear (36864 x 12288 INT4 row-wise weights, or
-INT8 ones with --codes int8, rotating over 5 matrices so every launch
-streams from HBM; prepacked or row-major layout) `reps` times at token
-count m, then a plain device-to-device copy of exactly 1 GiB (torch
-copy_) `reps` times.  The copy has a known HBM traffic (1 GiB read, 1 GiB
-written per launch), which calibrates what FETCH_SIZE / WRITE_SIZE report
-per byte on this GPU.
+decode   the decode QKV linear (36864 x 12288 INT4 row-wise weights, or INT8
+         ones with --codes int8; prepacked or row-major) `reps` times at token
+         count m, rotating over 5 matrices so every launch streams from HBM.
+prefill  the prefill GEMMs at M = 2048 tokens on prepacked weights:
+         attention-out 12288 x 12288, then the fused GeGLU FFN-up
+         65536 x 12288 (--which selects one), `reps` times each.
+step     the decode step of the benchmark's headline workload: QKV at
+         M = 1, 8, 32, 64, one launch each, back to back, `reps` times.
+Each mode ends with a plain device-to-device copy of exactly 1 GiB (torch
+copy_) `reps` times, whose HBM traffic is known (1 GiB read and 1 GiB
+written per launch): it calibrates what FETCH_SIZE / WRITE_SIZE report per
+byte, and its kernel marks the end of the sequence in a trace.
+
+summarize-pmc reads the counter CSVs of one or more rocprofv3 --pmc runs
+and prints, per kernel, the mean of every counter per dispatch;
+summarize-trace reads a --kernel-trace CSV and prints the per-kernel
+durations and, for the step mode, the gaps between consecutive launches.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import os
 import sys
+from collections import OrderedDict, defaultdict
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--m", type=int, default=64)
-    ap.add_argument("--reps", type=int, default=10)
-    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
-    ap.add_argument("--layout", choices=("prepacked", "row-major"), default="prepacked")
-    ap.add_argument("--codes", choices=("int4", "int8"), default="int4")
-    a = ap.parse_args(argv)
-
-    import torch
-    import weight_only_int4_rowwise_amd as w4
-    from weight_only_int4_rowwise_amd import synth
-
-    dev = "cuda:0"
+def _decode(a, torch, w4, synth, dev):
     n, k = synth.QKV_OUT, synth.HIDDEN
     qs = []
     int8 = a.codes == "int8"
@@ -42,7 +48,8 @@ def main(argv=None):
     y = torch.empty(a.m, n, dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
     print(f"decode QKV m={a.m} ({a.codes}, {a.layout}): {a.reps} launches", flush=True)
-    lin, lin_p = (w4.w8a16_linear, w4.w8a16_linear_prepacked) if int8 else (w4.w4a16_linear, w4.w4a16_linear_prepacked)
+    lin, lin_p = ((w4.w8a16_linear, w4.w8a16_linear_prepacked) if int8
+                  else (w4.w4a16_linear, w4.w4a16_linear_prepacked))
     for r in range(a.reps):
         q, s, qp = qs[r % 5]
         if a.layout == "prepacked":
@@ -50,6 +57,61 @@ def main(argv=None):
         else:
             lin(x, q, s, y_out=y)
     torch.cuda.synchronize()
+
+
+def _prefill(a, torch, w4, synth, dev):
+    M, H, F = synth.SEQ, synth.HIDDEN, synth.FFN
+    g = synth.generator(300, dev)
+    x = synth.activations(M, H, g, dev)
+    if a.which in ("all", "attn_out"):
+        w = synth.weight(H, H, g, device=dev)
+        q, s = w4.quantize_rowwise_int4(w)
+        qp = w4.w4a16_prepack(q)
+        del w, q
+        y = torch.empty(M, H, dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        print(f"prefill attention-out {H}x{H} M={M}: {a.reps} launches", flush=True)
+        for _ in range(a.reps):
+            w4.w4a16_linear_prepacked(x, qp, s, y_out=y)
+        torch.cuda.synchronize()
+        del qp, s, y
+    if a.which in ("all", "ffn_up_geglu"):
+        w = synth.weight(2 * F, H, g, device=dev)
+        q, s = w4.quantize_rowwise_int4(w)
+        qp = w4.w4a16_prepack(q)
+        del w, q
+        y = torch.empty(M, F, dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        print(f"prefill FFN-up GeGLU {2 * F}x{H} M={M}: {a.reps} launches", flush=True)
+        for _ in range(a.reps):
+            w4.w4a16_geglu_linear_prepacked(x, qp, s, y_out=y)
+        torch.cuda.synchronize()
+
+
+def _step(a, torch, w4, synth, dev):
+    n, k = synth.QKV_OUT, synth.HIDDEN
+    qs = []
+    for i in range(5):
+        w = synth.weight(n, k, synth.generator(10 + i, dev), device=dev)
+        q, s = w4.quantize_rowwise_int4(w)
+        qs.append((w4.w4a16_prepack(q), s))
+        del w, q
+    g = synth.generator(0, dev)
+    ms = (1, 8, 32, 64)
+    xs = {m: synth.activations(m, k, g, dev) for m in ms}
+    ys = {m: torch.empty(m, n, dtype=torch.float16, device=dev) for m in ms}
+    torch.cuda.synchronize()
+    print(f"decode step QKV M = {ms}: {a.reps} steps", flush=True)
+    i = 0
+    for _ in range(a.reps):
+        for m in ms:
+            qp, s = qs[i % 5]
+            i += 1
+            w4.w4a16_linear_prepacked(xs[m], qp, s, y_out=ys[m])
+    torch.cuda.synchronize()
+
+
+def _copy(a, torch, dev):
     src = torch.empty(a.copy_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -58,6 +120,95 @@ def main(argv=None):
     for _ in range(a.reps):
         dst.copy_(src)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- summaries
+
+def _csv_rows(pattern_dirs, suffix):
+    rows = []
+    for d in pattern_dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+            with open(path, newline="") as fh:
+                rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_pmc(dirs):
+    """Mean of each counter per dispatch, per kernel, over the counter CSVs
+    (rocprofv3 writes one row per dispatch and counter)."""
+    acc = defaultdict(lambda: defaultdict(list))
+    for r in _csv_rows(dirs, "counter_collection.csv"):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = OrderedDict()
+    for kern, counters in acc.items():
+        out[kern] = {c: (sum(v) / len(v), len(v)) for c, v in counters.items()}
+    return out
+
+
+def summarize_trace(d):
+    """Per-kernel durations of a --kernel-trace run, and the launch order
+    with start / end times (ns) for gap analysis."""
+    rows = _csv_rows([d], "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    seq = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    return seq
+
+
+def _print_pmc(dirs):
+    for kern, counters in summarize_pmc(dirs).items():
+        print(kern)
+        for c, (mean, n) in sorted(counters.items()):
+            print(f"    {c:32s} {mean:16.1f}   ({n} dispatches)")
+
+
+def _print_trace(d):
+    seq = summarize_trace(d)
+    per = defaultdict(list)
+    for name, s, e in seq:
+        per[name].append((e - s) / 1e3)
+    for name, v in per.items():
+        print(f"{len(v):6d} calls  avg {sum(v) / len(v):9.2f} us  min {min(v):9.2f}  max {max(v):9.2f}  {name}")
+    print("launch sequence (us): kernel, duration, gap after the previous launch's end")
+    prev = None
+    for name, s, e in seq:
+        gap = "" if prev is None else f"{(s - prev) / 1e3:8.2f}"
+        print(f"  {(e - s) / 1e3:9.2f} {gap:>8s}  {name[:90]}")
+        prev = e
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="mode", required=True)
+    for mode in ("decode", "prefill", "step"):
+        p = sub.add_parser(mode)
+        p.add_argument("--reps", type=int, default=10)
+        p.add_argument("--copy-bytes", type=int, default=1 << 30)
+        if mode == "decode":
+            p.add_argument("--m", type=int, default=64)
+            p.add_argument("--layout", choices=("prepacked", "row-major"), default="prepacked")
+            p.add_argument("--codes", choices=("int4", "int8"), default="int4")
+        if mode == "prefill":
+            p.add_argument("--which", choices=("all", "attn_out", "ffn_up_geglu"), default="all")
+    p = sub.add_parser("summarize-pmc")
+    p.add_argument("dirs", nargs="+")
+    p = sub.add_parser("summarize-trace")
+    p.add_argument("dir")
+    a = ap.parse_args(argv)
+
+    if a.mode == "summarize-pmc":
+        _print_pmc(a.dirs)
+        return 0
+    if a.mode == "summarize-trace":
+        _print_trace(a.dir)
+        return 0
+
+    import torch
+    import weight_only_int4_rowwise_amd as w4
+    from weight_only_int4_rowwise_amd import synth
+
+    dev = "cuda:0"
+    {"decode": _decode, "prefill": _prefill, "step": _step}[a.mode](a, torch, w4, synth, dev)
+    _copy(a, torch, dev)
     print("done", flush=True)
     return 0
 
