@@ -53,10 +53,16 @@ def linear_bytes(m, n_rows, k, n_out):
     return n_rows * k // 2 + 2 * n_rows + 2 * m * k + 2 * m * n_out
 
 
-def csrc_hash():
+# the sources the INT4 decode kernel is built from (its template, its
+# instantiation unit, the shared device helpers and the dispatching ABI)
+DECODE_SOURCES = ("api.hip", "common.hpp", "decode.hip", "decode.hpp")
+
+
+def csrc_hash(names=None):
+    """sha256 prefix over the library sources `names` (default: all of csrc/)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "weight_only_int4_rowwise_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in sorted(names or os.listdir(d)):
         with open(os.path.join(d, name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
@@ -81,6 +87,25 @@ def time_launches(torch, fn, reps, warm=2, repeats=5):
         e.synchronize()
         times.append(s.elapsed_time(e) / 1e3 / reps)
     return sorted(times)[len(times) // 2]
+
+
+def settle(torch, fn, ms):
+    """Runs fn back to back until `ms` of GPU time have passed (checked every
+    10 calls); returns the time spent.  After idle the GPU's clocks go
+    through a transient of some tens of milliseconds under load (kernels up
+    to 1.5x slower 2-10 ms in, then back), so everything timed here starts
+    from the sustained state."""
+    spent = 0.0
+    while spent < ms:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        e1.synchronize()
+        spent += e0.elapsed_time(e1)
+    return spent
 
 
 def make_rotating(torch, w4, synth, n, k, dist, count, seed0, dev):
@@ -124,6 +149,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-full-step", action="store_true", help="skip the 70-layer decode step")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="GPU time of back-to-back steps run before anything is timed")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -159,6 +186,8 @@ def main(argv=None):
             it[0] += 1
             w4.w4a16_linear_prepacked(xs[m], qp, s, y_out=ys[m])
 
+    settled_ms = settle(torch, step, a.settle_ms)
+    log(f"clocks settled: {settled_ms:.0f} ms of back-to-back steps before timing")
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -174,7 +203,27 @@ def main(argv=None):
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"headline: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
-    # per-M launch durations (roofline of the dominant decode launch), both layouts
+    # each launch of the step timed by its own events, over another K steps
+    # (a separate loop, so the headline loop above has no events between its launches)
+    in_step = {m: [] for m in DECODE_MS}
+    evs = []
+    for _ in range(a.steps):
+        for m in DECODE_MS:
+            _, s_, qp = qkv[it[0] % ROTATE]
+            it[0] += 1
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            w4.w4a16_linear_prepacked(xs[m], qp, s_, y_out=ys[m])
+            e1.record()
+            evs.append((m, e0, e1))
+    torch.cuda.synchronize()
+    for m, e0, e1 in evs:
+        in_step[m].append(e0.elapsed_time(e1) / 1e3)
+    in_step_us = {m: sum(v) / len(v) * 1e6 for m, v in in_step.items()}
+    log("launch durations within the step (us): " + ", ".join(f"M={m}: {t:.1f}" for m, t in in_step_us.items()))
+
+    # per-M launch durations in isolation (each M back to back), both layouts
     per_m, per_m_rm = {}, {}
     for m in DECODE_MS:
         for layout, table in (("prepacked", per_m), ("row-major", per_m_rm)):
@@ -194,59 +243,52 @@ def main(argv=None):
                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
                         "mfma_frac_needed": round(2.0 * m * N * K / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
             log(f"decode QKV M={m} {layout}: {t * 1e6:.1f} us, {b / t / 1e9:.0f} GB/s")
-    dom = max(DECODE_MS, key=lambda m: per_m[m]["us"])
+    dom = max(DECODE_MS, key=lambda m: in_step_us[m])
+    dom_bytes = linear_bytes(dom, N, K, N)
+    dom_gbs = dom_bytes / (in_step_us[dom] / 1e6) / 1e9
     mb = (dom + 15) // 16
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "decode_qkv_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tr = json.load(fh)
-        if tr.get("csrc_hash") == csrc_hash() and str(dom) in tr.get("bytes_per_launch", {}):
+        if tr.get("decode_source_hash") == csrc_hash(DECODE_SOURCES) and \
+                str(dom) in tr.get("bytes_per_launch", {}):
             traffic = tr["bytes_per_launch"][str(dom)]
     roofline = {
         "bound": "hbm",
         "kernel": f"decode_kernel, M={dom} ({mb} token block{'s' if mb > 1 else ''}), prepacked "
                   "QKV 36864x12288",
-        "achieved": per_m[dom]["GBs"],
+        "achieved": round(dom_gbs, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(per_m[dom]["GBs"] / HBM_PEAK_GBS, 4),
+        "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "algorithmic_bytes_per_launch": per_m[dom]["bytes"],
-        "avg_launch_us": per_m[dom]["us"],
+        "algorithmic_bytes_per_launch": dom_bytes,
+        "avg_launch_us": round(in_step_us[dom], 2),
+        "launches_timed": len(in_step[dom]),
+        "timing": "events around each launch of the step, over K steps after the timed headline loop",
     }
 
     # ------------------------------------------------------- cpu baseline
     cpu = None
+    cpu_configs = None
     if not a.no_cpu_baseline:
-        import oracle
-        rows = 24576          # two thirds of the QKV rows: about 10-20 s of CPU work
-        q0, s0, _ = qkv[0]
-        p_host = q0[:rows].cpu().numpy()
-        s_host = s0[:rows].cpu().view(torch.int16).numpy().view("uint16")
-        tot_b, tot_t = 0, 0.0
-        for m in DECODE_MS:
-            xh = xs[m].cpu().view(torch.int16).numpy().view("uint16")
-            c0 = time.perf_counter()
-            oracle.linear(xh, p_host, s_host)
-            tot_t += time.perf_counter() - c0
-            tot_b += linear_bytes(m, rows, K, rows)
-        cpu = {"value": round(tot_b / tot_t / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
-               "sample": f"oracle.linear (fp64, plain loops, OpenMP over outputs) on the first {rows} of "
-                         f"{N} QKV rows at M = 1, 8, 32, 64 ({tot_t:.1f} s of CPU time); "
-                         "same algorithmic-byte accounting as value"}
-        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads")
+        cpu, cpu_configs = cpu_baselines(torch, synth, dev, xs)
 
     # -------------------------------------------------------------- extra
     tot_b = sum(per_m_rm[m]["bytes"] for m in DECODE_MS)
     tot_t = sum(per_m_rm[m]["us"] for m in DECODE_MS) / 1e6
-    extra = {"decode_qkv_per_m": {str(m): v for m, v in per_m.items()},
+    extra = {"decode_qkv_in_step_us": {str(m): round(t, 2) for m, t in in_step_us.items()},
+             "clock_settle_ms": round(settled_ms, 1),
+             "decode_qkv_per_m": {str(m): v for m, v in per_m.items()},
              "decode_qkv_row_major_per_m": {str(m): v for m, v in per_m_rm.items()},
              "decode_qkv_row_major_step_GBs": round(tot_b / tot_t / 1e9, 1)}
     del ys
+    if cpu_configs is not None:
+        extra["cpu_oracle_per_config"] = cpu_configs
     if not a.no_extra:
-        extra.update(extra_workloads(torch, w4, synth, dev, a))
+        extra.update(extra_workloads(torch, w4, synth, dev, a, qkv))
 
     out = {
         "metric": METRIC,
@@ -277,8 +319,201 @@ def main(argv=None):
     return 0
 
 
-def extra_workloads(torch, w4, synth, dev, a):
-    res = {}
+def cpu_model():
+    """The host CPU's model name (Linux), else what the platform module says."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baselines(torch, synth, dev, xs):
+    """The oracle as it stands (binary64, plain loops, OpenMP over outputs on
+    every thread it is given), timed by wall clock on bounded samples of each
+    workload, from the same seeded fp16 weights as the GPU runs (redrawn on
+    the GPU, copied to the host, quantized by the oracle itself).  Returns
+    (the headline entry: QKV decode, and one entry per workload)."""
+    import numpy as np
+    import oracle
+
+    def host(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def timed(fn, *args):
+        c0 = time.perf_counter()
+        out = fn(*args)
+        return out, time.perf_counter() - c0
+
+    H, F, N = synth.HIDDEN, synth.FFN, synth.QKV_OUT
+    threads = oracle.num_threads()
+    model = cpu_model()
+    res = {"cpu_model": model, "threads": threads,
+           "note": "wall-clock seconds of the oracle on the samples named; rates are the samples' "
+                   "algorithmic bytes or flops over that time, so they extrapolate to the full shape"}
+
+    # headline: QKV decode, the first `rows` rows of the first rotating weight
+    rows = 24576
+    w = synth.weight(N, H, synth.generator(10, dev), "normal", dev)[:rows]
+    (p, sc), tq = timed(oracle.quantize_rowwise_int4, host(w))
+    del w
+    tot_b, tot_t, per_m = 0, 0.0, {}
+    for m in DECODE_MS:
+        _, t = timed(oracle.linear, host(xs[m]), p, sc)
+        b = linear_bytes(m, rows, H, rows)
+        tot_b += b
+        tot_t += t
+        per_m[str(m)] = {"s": round(t, 3), "GBs": round(b / t / 1e9, 4)}
+    cpu = {"value": round(tot_b / tot_t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "cpu_model": model,
+           "sample": f"oracle.linear (fp64, plain loops, OpenMP over outputs) on the first {rows} of "
+                     f"{N} QKV rows at M = 1, 8, 32, 64: {tot_t:.1f} s of wall time on {threads} threads; "
+                     "same algorithmic-byte accounting as value"}
+    res["qkv_decode"] = {"rows_sampled": rows, "of_rows": N, "per_m": per_m,
+                         "GBs": cpu["value"], "quantize_s": round(tq, 3),
+                         "quantize_GBs": round(rows * (2 * H + H // 2 + 2) / tq / 1e9, 4)}
+    log(f"cpu baseline: {cpu['value']} GB/s on {threads} threads ({model})")
+
+    # toy: 1024 x 1024, M = 1 and 16, in full
+    wt, xt = synth.toy()
+    (pt, st), tq = timed(oracle.quantize_rowwise_int4, host(wt))
+    toy = {"quantize_us": round(tq * 1e6, 1)}
+    for m, x in xt.items():
+        _, t = timed(oracle.linear, host(x), pt, st)
+        toy[f"linear_m{m}_us"] = round(t * 1e6, 1)
+        toy[f"linear_m{m}_GBs"] = round(linear_bytes(m, 1024, 1024, 1024) / t / 1e9, 4)
+    res["toy_1024x1024"] = toy
+
+    # GeGLU decode: fused up-projection on 2048 of the 32768 gate/value row
+    # pairs, down on 2048 of its 12288 rows, t(4) weights, M = 1 and 16
+    fs = 2048
+    wu = synth.weight(2 * F, H, synth.generator(100, dev), "t4", dev)
+    wu = torch.cat([wu[:fs], wu[F:F + fs]])
+    pu, su = oracle.quantize_rowwise_int4(host(wu))
+    wd = synth.weight(H, F, synth.generator(200, dev), "t4", dev)[:fs]
+    pd, sd = oracle.quantize_rowwise_int4(host(wd))
+    del wu, wd
+    g = synth.generator(1, dev)
+    gd = {}
+    for m in (1, 16):
+        xu = synth.activations(m, H, g, dev)
+        xd = synth.activations(m, F, g, dev)
+        _, tu = timed(oracle.geglu, host(xu), pu, su)
+        _, td = timed(oracle.linear, host(xd), pd, sd)
+        gd[str(m)] = {"up_geglu_GBs": round(linear_bytes(m, 2 * fs, H, fs) / tu / 1e9, 4),
+                      "down_GBs": round(linear_bytes(m, fs, F, fs) / td / 1e9, 4)}
+    res["geglu_decode"] = {"sample": f"up: {fs} of {F} gate/value pairs; down: {fs} of {H} rows", "per_m": gd}
+
+    # prefill at M = 2048: the first 16 tokens through attention-out (all
+    # 12288 rows) and 8 tokens through the fused FFN-up on 4096 pairs;
+    # TFLOP/s of the sample, and the full call's time at that rate
+    wa = synth.weight(H, H, synth.generator(300, dev), "normal", dev)
+    pa, sa = oracle.quantize_rowwise_int4(host(wa))
+    del wa
+    x = synth.activations(16, H, synth.generator(301, dev), dev)
+    _, t = timed(oracle.linear, host(x), pa, sa)
+    fl = 2.0 * 16 * H * H
+    pf = {"attn_out": {"sample": "16 of 2048 tokens, all 12288 rows", "TFLOPs": round(fl / t / 1e12, 5),
+                       "extrapolated_full_s": round(t * synth.SEQ / 16, 2)}}
+    fs2 = 4096
+    wu = synth.weight(2 * F, H, synth.generator(100, dev), "t4", dev)
+    wu = torch.cat([wu[:fs2], wu[F:F + fs2]])
+    pu2, su2 = oracle.quantize_rowwise_int4(host(wu))
+    del wu
+    _, t = timed(oracle.geglu, host(x[:8]), pu2, su2)
+    fl = 2.0 * 8 * 2 * fs2 * H
+    pf["ffn_up_geglu"] = {"sample": f"8 of 2048 tokens, {fs2} of {F} gate/value pairs",
+                          "TFLOPs": round(fl / t / 1e12, 5),
+                          "extrapolated_full_s": round(t * (synth.SEQ / 8) * (F / fs2), 2)}
+    res["prefill_m2048"] = pf
+
+    # the 70-layer step at M = 8: one layer's four linears on 1/8 of their
+    # rows (seeds of layer 0), extrapolated to 8 x 70
+    g7 = synth.generator(7, dev)
+    xs8 = {k: synth.activations(8, k, g7, dev) for k in sorted({k for _, _, k in synth.LAYER_LINEARS})}
+    t_layer, b_layer = 0.0, 0
+    for mid, (name, n, k) in enumerate(synth.LAYER_LINEARS):
+        w = synth.weight(n, k, synth.generator(synth.layer_weight_seed(0, mid), dev), device=dev)
+        if name == "ffn_up":
+            f8 = n // 16
+            w = torch.cat([w[:f8], w[n // 2:n // 2 + f8]])
+            pl, sl = oracle.quantize_rowwise_int4(host(w))
+            _, t = timed(oracle.geglu, host(xs8[k]), pl, sl)
+            b_layer += linear_bytes(8, 2 * f8, k, f8)
+        else:
+            w = w[:n // 8]
+            pl, sl = oracle.quantize_rowwise_int4(host(w))
+            _, t = timed(oracle.linear, host(xs8[k]), pl, sl)
+            b_layer += linear_bytes(8, n // 8, k, n // 8)
+        del w
+        t_layer += t
+    res["full_decode_step_m8"] = {"sample": "layer 0, 1/8 of each linear's rows (GeGLU: of its pairs)",
+                                  "GBs": round(b_layer / t_layer / 1e9, 4),
+                                  "extrapolated_step_s": round(t_layer * 8 * synth.LAYERS, 1)}
+    log(f"cpu oracle per config: {res}")
+    return cpu, res
+
+
+def hbm_ceilings(torch, dev):
+    """Context ceilings for the HBM-bound kernels, through torch: a 1 GiB
+    device-to-device copy (read + write) and a read-only reduction (amax)
+    over 1 GiB of fp16."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    settle(torch, lambda: dst.copy_(src), 60.0)       # after the CPU leg the GPU was idle
+    t = time_launches(torch, lambda: dst.copy_(src), 10)
+    r = {"copy_1GiB": {"us": round(t * 1e6, 1), "GBs_read_plus_write": round(2 * nbytes / t / 1e9, 1)}}
+    del dst
+    h = src.view(torch.float16)
+    t = time_launches(torch, lambda: torch.amax(h), 10)
+    r["amax_read_1GiB"] = {"us": round(t * 1e6, 1), "GBs_read": round(nbytes / t / 1e9, 1)}
+    del src, h
+    torch.cuda.empty_cache()
+    log(f"HBM ceilings (torch): {r}")
+    return r
+
+
+def intermediate_m(torch, w4, synth, dev, mats, g):
+    """Batched decode between the decode and prefill configurations: QKV,
+    attention-out and the fused GeGLU up-projection at m = 96 ... 384 tokens
+    (64 < m <= 128 runs the decode kernel twice, larger m the prefill GEMM),
+    prepacked, with both the HBM and the MFMA fraction of each launch."""
+    H = synth.HIDDEN
+    out = {}
+    for name, (rot, n_rows, k, geglu) in mats.items():
+        n_out = n_rows // 2 if geglu else n_rows
+        row = {}
+        for m in (96, 128, 192, 256, 384):
+            x = synth.activations(m, k, g, dev)
+            y = torch.empty(m, n_out, dtype=torch.float16, device=dev)
+            c = [0]
+            fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+
+            def one(c=c, x=x, y=y, fn=fn, rot=rot):
+                _, s, qp = rot[c[0] % len(rot)]
+                c[0] += 1
+                fn(x, qp, s, y_out=y)
+
+            t = time_launches(torch, one, 10)
+            b = linear_bytes(m, n_rows, k, n_out)
+            fl = 2.0 * m * n_rows * k
+            row[str(m)] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                           "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                           "TFLOPs": round(fl / t / 1e12, 1),
+                           "frac_mfma": round(fl / t / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+            del x, y
+        out[name] = row
+        log(f"intermediate m, {name}: {row}")
+    return out
+
+
+def extra_workloads(torch, w4, synth, dev, a, qkv):
+    res = {"hbm_ceilings_torch": hbm_ceilings(torch, dev)}
     H, F = synth.HIDDEN, synth.FFN
 
     # GeGLU decode: fused up-projection 65536 x 12288 and down 12288 x 32768, t(4) weights
@@ -373,6 +608,11 @@ def extra_workloads(torch, w4, synth, dev, a):
     del y6, x5
     res["prefill_m512"] = pf5
     log(f"prefill M=512: {pf5}")
+    res["intermediate_m"] = intermediate_m(
+        torch, w4, synth, dev,
+        {"qkv_36864x12288": (qkv, synth.QKV_OUT, H, False),
+         "attn_out_12288x12288": (attn, H, H, False),
+         "ffn_up_geglu_65536x12288": (ups, 2 * F, H, True)}, g)
     del ups, attn
 
     res["w8a16"] = int8_workloads(torch, w4, synth, dev, g)

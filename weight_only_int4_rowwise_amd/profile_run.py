@@ -14,7 +14,8 @@ prefill  the prefill GEMMs at M = 2048 tokens on prepacked weights:
          attention-out 12288 x 12288, then the fused GeGLU FFN-up
          65536 x 12288 (--which selects one), `reps` times each.
 step     the decode step of the benchmark's headline workload: QKV at
-         M = 1, 8, 32, 64, one launch each, back to back, `reps` times.
+         M = 1, 8, 32, 64 (or the --ms list), one launch each, back to
+         back, `reps` times.
 Each mode ends with a plain device-to-device copy of exactly 1 GiB (torch
 copy_) `reps` times, whose HBM traffic is known (1 GiB read and 1 GiB
 written per launch): it calibrates what FETCH_SIZE / WRITE_SIZE report per
@@ -97,7 +98,7 @@ def _step(a, torch, w4, synth, dev):
         qs.append((w4.w4a16_prepack(q), s))
         del w, q
     g = synth.generator(0, dev)
-    ms = (1, 8, 32, 64)
+    ms = tuple(int(v) for v in a.ms.split(","))
     xs = {m: synth.activations(m, k, g, dev) for m in ms}
     ys = {m: torch.empty(m, n, dtype=torch.float16, device=dev) for m in ms}
     torch.cuda.synchronize()
@@ -135,14 +136,47 @@ def _csv_rows(pattern_dirs, suffix):
 
 def summarize_pmc(dirs):
     """Mean of each counter per dispatch, per kernel, over the counter CSVs
-    (rocprofv3 writes one row per dispatch and counter)."""
+    (rocprofv3 writes one row per dispatch and counter); the pseudo-counter
+    DURATION_NS is the mean dispatch duration from the rows' timestamps."""
     acc = defaultdict(lambda: defaultdict(list))
     for r in _csv_rows(dirs, "counter_collection.csv"):
         acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        acc[r["Kernel_Name"]]["DURATION_NS"].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
     out = OrderedDict()
     for kern, counters in acc.items():
         out[kern] = {c: (sum(v) / len(v), len(v)) for c, v in counters.items()}
     return out
+
+
+# gfx950 as a rocprofv3 run sees it: GRBM_GUI_ACTIVE is summed over the 8
+# XCDs; SQ_* cycle counters over all compute units or SIMDs as noted
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def derived(counters):
+    """Per-dispatch utilisations from the mean counters of one kernel."""
+    c = {k: v[0] for k, v in counters.items()}
+    cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS            # kernel cycles (each XCD's clock)
+    d = {"duration_us": c.get("DURATION_NS", 0.0) / 1e3, "cycles": cyc}
+    if cyc and c.get("DURATION_NS"):
+        d["clock_GHz"] = cyc / c["DURATION_NS"]
+    if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        d["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c["SQ_VALU_MFMA_BUSY_CYCLES"]:
+            d["mfma_cycles_with_valu"] = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"]
+    if cyc and "SQ_INSTS_VALU" in c:
+        valu = c["SQ_INSTS_VALU"] - c.get("SQ_INSTS_MFMA", 0.0)    # SQ_INSTS_VALU counts MFMAs too
+        d["valu_insts_per_simd"] = valu / SIMDS
+        d["valu_busy"] = 4.0 * valu / SIMDS / cyc                   # a wave64 VALU op takes 4 cycles
+    if cyc and "SQ_LDS_IDX_ACTIVE" in c:
+        d["lds_busy"] = c["SQ_LDS_IDX_ACTIVE"] / (cyc * CUS)
+        if c["SQ_LDS_IDX_ACTIVE"]:
+            d["lds_bank_conflict_share"] = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"]
+    if cyc and "TA_TA_BUSY" in c:
+        d["ta_busy"] = c["TA_TA_BUSY"] / (cyc * CUS)
+    if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+        d["wave_cycles_waiting"] = c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+    return d
 
 
 def summarize_trace(d):
@@ -152,6 +186,24 @@ def summarize_trace(d):
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     seq = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
     return seq
+
+
+def traffic(fetch_dir, write_dir, kernel_part, copy_bytes=1 << 30):
+    """HBM bytes per dispatch of the kernel whose name contains kernel_part,
+    from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each
+    scaled by what the counter reads for the 1 GiB device copy of the same
+    run (1 GiB read and 1 GiB written per dispatch)."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = summarize_pmc([d])
+        kern = [v[counter][0] for k, v in per.items() if kernel_part in k and counter in v]
+        copy = [v[counter][0] for k, v in per.items() if "copyBuffer" in k and counter in v]
+        if len(kern) != 1 or len(copy) != 1:
+            raise RuntimeError(f"{counter}: expected one matching kernel and one copy in {d}")
+        factor = copy_bytes / (copy[0] * 1024)
+        out[counter] = {"kib_per_dispatch": kern[0], "copy_kib_per_dispatch": copy[0],
+                        "factor": factor, "bytes": kern[0] * 1024 * factor}
+    return out
 
 
 def _print_pmc(dirs):
@@ -189,11 +241,32 @@ def main(argv=None):
             p.add_argument("--codes", choices=("int4", "int8"), default="int4")
         if mode == "prefill":
             p.add_argument("--which", choices=("all", "attn_out", "ffn_up_geglu"), default="all")
+        if mode == "step":
+            p.add_argument("--ms", default="1,8,32,64", help="token counts of one step, in launch order")
     p = sub.add_parser("summarize-pmc")
     p.add_argument("dirs", nargs="+")
     p = sub.add_parser("summarize-trace")
     p.add_argument("dir")
+    p = sub.add_parser("derived")
+    p.add_argument("kernel_part")
+    p.add_argument("dirs", nargs="+")
+    p = sub.add_parser("traffic")
+    p.add_argument("fetch_dir")
+    p.add_argument("write_dir")
+    p.add_argument("kernel_part")
     a = ap.parse_args(argv)
+
+    if a.mode == "derived":
+        for kern, counters in summarize_pmc(a.dirs).items():
+            if a.kernel_part in kern:
+                print(kern.split("(")[0])
+                for k, v in derived(counters).items():
+                    print(f"    {k:24s} {v:12.4f}")
+        return 0
+    if a.mode == "traffic":
+        import json
+        print(json.dumps(traffic(a.fetch_dir, a.write_dir, a.kernel_part), indent=1))
+        return 0
 
     if a.mode == "summarize-pmc":
         _print_pmc(a.dirs)
