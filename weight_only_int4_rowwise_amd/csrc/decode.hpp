@@ -512,7 +512,8 @@ void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const 
 // the grid still covers the 256 CUs (below about 8192 rows: 16 or 32 rows),
 // and more reduction splits (more wavefronts per row); a short reduction
 // (k <= 4096) wants a short round (128 or 256 columns per K-part), or the
-// ring never fills.  More token blocks want more row groups per wavefront
+// ring never fills; a long one (the 32768-column FFN-down at m <= 8) wants
+// three row groups per wavefront and eight K-parts (36.8 against 38.7 us).  More token blocks want more row groups per wavefront
 // (each activation operand feeds more MFMAs).  At m > 48 tall weights keep
 // three weight register sets in flight (D = 3): the round there is long
 // enough that two sets leave the wave waiting on the loads.
@@ -544,7 +545,7 @@ hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *pa
             : b    ? W4_DEC(2, 2, 8, 2, 1, 16, 2)
                    : W4_DEC(2, 1, 8, 2, 1, 16, 2);
         else if (m <= 32)
-            b == 3   ? W4_DEC(1, 4, 16, 2, 2, 32, 4)
+            b == 3   ? W4_DEC(1, 4, 8, 2, 2, 32, 4)
             : b == 2 ? W4_DEC(2, 2, 4, 2, 2, 32, 4)
             : b == 1 ? W4_DEC(2, 2, 8, 2, 2, 32, 2)
                      : W4_DEC(2, 1, 4, 2, 2, 32, 2);
@@ -569,7 +570,9 @@ hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *pa
         else if (m <= 8)
             b == 4   ? W4_DEC(2, 4, 4, 2, 1, 8, 1)
             : b >= 2 ? W4_DEC(1, 1, 4, 2, 1, 8, 3)
-            : b == 1 ? (k < 4096 ? W4_DEC(1, 1, 4, 2, 1, 8, 1) : W4_DEC(4, 3, 12, 2, 1, 8, 1))
+            : b == 1 ? (k < 4096    ? W4_DEC(1, 1, 4, 2, 1, 8, 1)
+                        : k >= 24576 ? W4_DEC(2, 1, 8, 2, 1, 8, 3)
+                                     : W4_DEC(4, 3, 12, 2, 1, 8, 1))
                      : W4_DEC(2, 2, 8, 2, 1, 8, 1);
         else if (m <= 16)
             b == 4                  ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
