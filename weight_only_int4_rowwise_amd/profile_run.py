@@ -213,16 +213,30 @@ def _print_pmc(dirs):
             print(f"    {c:32s} {mean:16.1f}   ({n} dispatches)")
 
 
-def _print_trace(d):
-    seq = summarize_trace(d)
+def trace_stats(d, name_part=""):
+    """Per-kernel call count, mean, median, min and max duration (us) of a
+    --kernel-trace run, for kernels whose name contains name_part."""
     per = defaultdict(list)
-    for name, s, e in seq:
-        per[name].append((e - s) / 1e3)
+    for name, s, e in summarize_trace(d):
+        if name_part in name:
+            per[name].append((e - s) / 1e3)
+    out = OrderedDict()
     for name, v in per.items():
-        print(f"{len(v):6d} calls  avg {sum(v) / len(v):9.2f} us  min {min(v):9.2f}  max {max(v):9.2f}  {name}")
+        v = sorted(v)
+        out[name] = {"calls": len(v), "mean": sum(v) / len(v), "median": v[len(v) // 2],
+                     "min": v[0], "max": v[-1]}
+    return out
+
+
+def _print_trace(d, sequence=False):
+    for name, st in trace_stats(d).items():
+        print(f"{st['calls']:6d} calls  mean {st['mean']:9.2f} us  median {st['median']:9.2f}  "
+              f"min {st['min']:9.2f}  max {st['max']:9.2f}  {name}")
+    if not sequence:
+        return
     print("launch sequence (us): kernel, duration, gap after the previous launch's end")
     prev = None
-    for name, s, e in seq:
+    for name, s, e in summarize_trace(d):
         gap = "" if prev is None else f"{(s - prev) / 1e3:8.2f}"
         print(f"  {(e - s) / 1e3:9.2f} {gap:>8s}  {name[:90]}")
         prev = e
@@ -247,6 +261,7 @@ def main(argv=None):
     p.add_argument("dirs", nargs="+")
     p = sub.add_parser("summarize-trace")
     p.add_argument("dir")
+    p.add_argument("--sequence", action="store_true", help="also list every launch in order")
     p = sub.add_parser("derived")
     p.add_argument("kernel_part")
     p.add_argument("dirs", nargs="+")
@@ -272,7 +287,7 @@ def main(argv=None):
         _print_pmc(a.dirs)
         return 0
     if a.mode == "summarize-trace":
-        _print_trace(a.dir)
+        _print_trace(a.dir, a.sequence)
         return 0
 
     import torch
