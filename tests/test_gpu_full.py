@@ -81,6 +81,25 @@ def test_qkv_two_decode_launches_sampled(qkv):
     print(f"QKV M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
+def test_qkv_prefill_m1024_sampled(qkv):
+    """QKV at m = 1024 runs 256-row x 64-token tiles (the 128-token grid
+    would leave half the CUs idle in its last wave): one token in every
+    64-token tile and two columns in every 256-row tile, a quarter of that
+    sample against the oracle."""
+    q, s, p_ref, s_ref, _ = qkv
+    m = 1024
+    x = synth.activations(m, synth.HIDDEN, synth.generator(8, DEV), DEV)
+    announce("QKV prefill", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(m, q.shape[0], 64, 256, 9)
+    keep = np.random.default_rng(10).random(mi.size) < 0.25
+    mi, ni = mi[keep], ni[keep]
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"QKV prefill M={m}")
+    print(f"QKV prefill M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 @pytest.fixture(scope="module")
 def ffn():
     w_up, w_down, x_up, x_down = synth.geglu_decode(device=DEV)
@@ -177,6 +196,8 @@ def prefill_data():
 
 
 def test_prefill_attn_out_sampled(prefill_data):
+    """Attention-out at m = 2048: 256-row x 128-token tiles (768 of them,
+    a last wave of one workgroup per CU)."""
     (q, s, p_ref, s_ref), _, x = prefill_data
     announce("prefill attn-out", tuple(x.shape))
     y = w4.w4a16_linear(x, q, s)

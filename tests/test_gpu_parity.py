@@ -416,7 +416,7 @@ def test_prefill_64_token_tiles(geglu):
 def test_prefill_large_grids(geglu, m, n, k):
     """Grids of more than two 256-row x 128-token tiles per CU (on a
     256-CU MI355X) take the 256-row tiles: 12280 rows at m = 2000 with
-    64-token tiles (768 large tiles fill 1.5 waves), 16380 rows with
+    64-token tiles (768 large tiles fill 1.5 waves, and k is short), 16380 rows with
     128-token tiles (1024 fill 2 waves), and GeGLU with 128-token tiles
     (f = 4080: ragged against 128-output tiles, a multiple of 16 as the
     prepacked GeGLU layout requires).  Ragged tokens and k; both layouts."""

@@ -329,8 +329,15 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //    against 467 us; QKV 36864 x 12288 at m = 256: 207 against 282 us);
     //    a grid that fills one wave exactly keeps the large tile (plain
     //    FFN-up 65536 x 12288 at m = 256: 331 against 371 us);
-    //  * larger plain grids keep 128-token tiles unless they would fill the
-    //    last wave of workgroups much worse than 64-token tiles (k <= 16384);
+    //  * larger plain grids keep 128-token tiles unless 64-token tiles fill
+    //    the last wave of workgroups much better (k <= 16384) and the
+    //    128-token grid's last wave would leave at least half the CUs idle
+    //    (QKV at m = 1024: 736 against 746 us), or the reduction is short
+    //    (k < 4096).  A last wave that gives each CU one workgroup costs
+    //    little, since those workgroups run with the CU to themselves:
+    //    attention-out 12288 x 12288 at m = 2048 runs 470-476 us on
+    //    128-token tiles against 484-486 us on 64-token tiles, QKV at
+    //    m = 1536 1037-1040 against 1089-1091 us;
     //  * larger GeGLU grids take 128-token tiles.
     //  * INT8 codes need a second weight register set per row group, so
     //    their large tiles keep 128 tokens with one row group fewer per
@@ -362,7 +369,8 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
         if (4 * g48 <= 9 * cus && fill8 < 0.9)
             return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
-        if (k <= 16384 && fill4 > fill8 + 0.1)
+        const int64_t last = g48 % slots;             // workgroups of a partial last wave
+        if (k <= 16384 && fill4 > fill8 + 0.1 && ((last > 0 && 2 * last <= cus) || k < 4096))
             return launch_prefill_t<4, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
         return launch_prefill_t<4, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     }
