@@ -69,10 +69,18 @@ def csrc_hash(names=None):
     return h.hexdigest()[:16]
 
 
+# GPU time every timed block first spends running its own launches back to
+# back (--settle-ms): blocks that follow setup work (quantizing, copies,
+# host-side preparation) would otherwise start inside the post-idle clock dip
+SETTLE_MS = 60.0
+
+
 def time_launches(torch, fn, reps, warm=2, repeats=5):
     """Duration (s) of one fn() call: the median over `repeats` timings of
     reps back-to-back launches each, timed with events on the current stream
-    (the stream the kernels run on)."""
+    (the stream the kernels run on), after fn has run back to back for
+    SETTLE_MS of GPU time."""
+    settle(torch, fn, SETTLE_MS)
     for _ in range(warm):
         fn()
     times = []
@@ -150,8 +158,10 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-full-step", action="store_true", help="skip the 70-layer decode step")
     ap.add_argument("--settle-ms", type=float, default=60.0,
-                    help="GPU time of back-to-back steps run before anything is timed")
+                    help="GPU time of back-to-back launches run before each timed block")
     a = ap.parse_args(argv)
+    global SETTLE_MS
+    SETTLE_MS = a.settle_ms
 
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); "
@@ -616,7 +626,7 @@ def extra_workloads(torch, w4, synth, dev, a, qkv):
     del ups, attn
 
     res["w8a16"] = int8_workloads(torch, w4, synth, dev, g)
-    res["w4a16_zp"] = zp_workloads(torch, w4, synth, dev, g)
+    res["w4a16_zp"] = zp_workloads(torch, w4, synth, dev, g, qkv)
 
     # quantizer: QKV-shaped fp16 weight -> packed + scales
     log("quantizer")
@@ -664,10 +674,12 @@ def linear_bytes_zp(m, n_rows, k, n_out):
     return linear_bytes(m, n_rows, k, n_out) + n_rows
 
 
-def zp_workloads(torch, w4, synth, dev, g):
+def zp_workloads(torch, w4, synth, dev, g, qkv4):
     """The zero-point INT4 variant at the GLM-130B shapes: QKV decode per M,
     the fused GeGLU up-projection at M = 1 and 16, and attention-out prefill
-    at M = 2048, all prepacked."""
+    at M = 2048, all prepacked; and QKV decode per M timed alternately with
+    the symmetric INT4 kernel on its own weights (qkv4: the headline's
+    rotating weights), three rounds each, the fastest of each kind kept."""
     log("zero-point INT4 workloads")
     H, F, N = synth.HIDDEN, synth.FFN, synth.QKV_OUT
 
@@ -701,6 +713,30 @@ def zp_workloads(torch, w4, synth, dev, g):
                          "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
     r["decode_qkv_per_m"] = per_m
     log(f"zero-point QKV decode: {per_m}")
+    ab = {}
+    for m in DECODE_MS:
+        x = synth.activations(m, H, g, dev)
+        y = torch.empty(m, N, dtype=torch.float16, device=dev)
+        c = [0, 0]
+
+        def zp_one(c=c, x=x, y=y):
+            qp, s, z = qkv[c[0] % len(qkv)]
+            c[0] += 1
+            w4.w4a16_zp_linear_prepacked(x, qp, s, z, y_out=y)
+
+        def int4_one(c=c, x=x, y=y):
+            _, s, qp = qkv4[c[1] % len(qkv4)]
+            c[1] += 1
+            w4.w4a16_linear_prepacked(x, qp, s, y_out=y)
+
+        t4, tz = [], []
+        for _ in range(3):
+            t4.append(time_launches(torch, int4_one, 30))
+            tz.append(time_launches(torch, zp_one, 30))
+        ab[str(m)] = {"int4_us": round(min(t4) * 1e6, 2), "zero_point_us": round(min(tz) * 1e6, 2),
+                      "ratio": round(min(tz) / min(t4), 4)}
+    r["decode_qkv_alternating_with_int4"] = ab
+    log(f"zero-point against INT4, alternating: {ab}")
     del qkv
     ups = rotating(2 * F, H, "t4", 3, 950)
     gd = {}
