@@ -488,6 +488,44 @@ def hbm_ceilings(torch, dev):
     return r
 
 
+def read_probe_table(torch, w4, dev):
+    """The library's streaming-read probe (w4a16_read_probe) at the byte
+    counts of the GLM-130B decode launches (attention-out, FFN-down, QKV,
+    FFN-up, at M = 8) and at 800 MiB, each launch on a fresh region of a
+    4 GiB arena so nothing is served from the caches; and a least-squares
+    fit time = fixed + bytes / rate over those sizes: the read ceiling and
+    the fixed cost of one launch of a bare stream."""
+    arena_bytes = 4 << 30
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device=dev).fill_(0x5A)
+    sink = torch.empty(1, dtype=torch.int32, device=dev)
+    sizes = {"attn_out_m8": 75_497_472, "ffn_down_m8": 201_326_592, "qkv_m8": 226_492_416,
+             "ffn_up_m8": 402_653_184, "800MiB": 800 << 20}
+    out, pts = {}, []
+    for name, nb in sizes.items():
+        nb -= nb % 1024
+        pos = [0]
+
+        def one(nb=nb, pos=pos):
+            if pos[0] + nb > arena_bytes:
+                pos[0] = 0
+            w4.read_probe(arena[pos[0]:pos[0] + nb], nb, sink)
+            pos[0] += nb
+
+        t = time_launches(torch, one, max(10, min(100, int(4e9 // nb))))
+        out[name] = {"bytes": nb, "us": round(t * 1e6, 2), "GBs": round(nb / t / 1e9, 1)}
+        pts.append((nb, t))
+    n = len(pts)
+    mx = sum(b for b, _ in pts) / n
+    my = sum(t for _, t in pts) / n
+    slope = sum((b - mx) * (t - my) for b, t in pts) / sum((b - mx) ** 2 for b, _ in pts)
+    res = {"sizes": out, "fit_fixed_us": round((my - slope * mx) * 1e6, 2),
+           "fit_GBs": round(1 / slope / 1e9, 1)}
+    del arena
+    torch.cuda.empty_cache()
+    log(f"read probe: {res}")
+    return res
+
+
 def intermediate_m(torch, w4, synth, dev, mats, g):
     """Batched decode between the decode and prefill configurations: QKV,
     attention-out and the fused GeGLU up-projection at m = 96 ... 384 tokens
@@ -524,6 +562,7 @@ def intermediate_m(torch, w4, synth, dev, mats, g):
 
 def extra_workloads(torch, w4, synth, dev, a, qkv):
     res = {"hbm_ceilings_torch": hbm_ceilings(torch, dev)}
+    res["hbm_read_probe"] = read_probe_table(torch, w4, dev)
     H, F = synth.HIDDEN, synth.FFN
 
     # GeGLU decode: fused up-projection 65536 x 12288 and down 12288 x 32768, t(4) weights

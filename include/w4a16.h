@@ -170,6 +170,17 @@ w4a16_status w4a16_geglu_linear_prepacked(const void *x_fp16, int64_t m, int64_t
                                           int64_t f, const void *bias_fp16, void *y_fp16,
                                           void *stream);
 
+/* Measurement utility, not a step of the method: reads `bytes` of device
+ * memory at `src` once (a multiple of 1024, 16-byte aligned, up to 2^40)
+ * in the plainest streaming pattern (one 768-thread workgroup per CU, each
+ * wavefront reading every W-th 1 KB block, W = all wavefronts, four loads
+ * in flight), so that a decode launch can be set beside what a bare stream
+ * of the same bytes costs on the same GPU.  `sink_u32` (4 bytes of device
+ * memory, 4-byte aligned) may receive one word; its content is meaningless.
+ * Stream-ordered on `stream`; allocates nothing.  Errors: W4A16_ERR_SHAPE,
+ * W4A16_ERR_NULL, W4A16_ERR_ALIGN, W4A16_ERR_HIP. */
+w4a16_status w4a16_read_probe(const void *src, int64_t bytes, void *sink_u32, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *w4a16_status_string(int status);
 

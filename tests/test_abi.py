@@ -252,3 +252,17 @@ def test_zp_linear_argument_checks(lib, fn):
     assert f(None, 1, 64, B, C, E, 16, None, D, None) == _lib.ERR_NULL
     assert f(A, 1, 48, B, C, E, 16, None, D, None) == _lib.ERR_SHAPE       # k % 32 != 0
     assert f(None, 0, 64, None, None, None, 16, None, None, None) == _lib.OK
+
+
+def test_read_probe_argument_checks(lib):
+    """The measurement probe rejects sizes that are not whole 1 KB blocks,
+    NULL and misaligned pointers; an empty read succeeds without a device."""
+    p = lib.w4a16_read_probe
+    assert p(A, -1024, B, None) == _lib.ERR_SHAPE
+    assert p(A, 1000, B, None) == _lib.ERR_SHAPE
+    assert p(A, (1 << 40) + 1024, B, None) == _lib.ERR_SHAPE
+    assert p(None, 0, None, None) == _lib.OK
+    assert p(None, 1024, B, None) == _lib.ERR_NULL
+    assert p(A, 1024, None, None) == _lib.ERR_NULL
+    assert p(MIS, 1024, B, None) == _lib.ERR_ALIGN
+    assert p(A, 1024, B + 2, None) == _lib.ERR_ALIGN

@@ -465,6 +465,24 @@ def test_deterministic_reruns():
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), m
 
 
+def test_read_probe_reads_without_writing():
+    """The streaming-read probe the benchmark uses (a measurement utility,
+    not a step of the method) reads whole 1 KB blocks, including a tail
+    shorter than one round of its wavefronts, and writes neither the buffer
+    nor (for data whose xor is not its constant) the sink."""
+    nbytes = (256 * 12 * 4 + 3) * 1024
+    buf = torch.zeros(nbytes + 4096, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 12345, dtype=torch.int32, device=DEV)
+    announce("read probe", nbytes)
+    w4.read_probe(buf, nbytes, sink)
+    w4.read_probe(buf, 1024, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 12345
+    assert int(buf.count_nonzero().item()) == 0
+    with pytest.raises(w4.W4A16Error):
+        w4.read_probe(buf, 1000, sink)
+
+
 def test_calls_follow_the_current_stream():
     """The binding passes torch's current stream; results on a side stream
     (default priority) equal those on the default stream."""

@@ -54,6 +54,7 @@ __all__ = [
     "w4a16_zp_geglu_linear",
     "w4a16_zp_linear_prepacked",
     "w4a16_zp_geglu_linear_prepacked",
+    "read_probe",
     "W4A16Error",
     "library",
 ]
@@ -495,3 +496,26 @@ def w4a16_zp_geglu_linear_prepacked(x, qp, s, z, bias=None, y_out=None):
                  None if bias is None else bias.data_ptr(), y_out.data_ptr())
     _lib.check(st, "w4a16_zp_geglu_linear_prepacked")
     return y_out
+
+
+def read_probe(buf, nbytes=None, sink=None):
+    """Measurement utility (not a step of the method): reads the first
+    `nbytes` (default: all; a multiple of 1024) of the device tensor `buf`
+    once in the plainest streaming pattern (w4a16_read_probe).  `sink`: an
+    int32 device tensor of at least one element, or None to allocate one."""
+    torch = _torch()
+    lib = _lib.load()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("read_probe: buf must be a contiguous GPU tensor")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes < 0 or nbytes > total:
+        raise ValueError(f"read_probe: nbytes {nbytes} outside the buffer's {total} bytes")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _require(sink, torch.int32, "sink")
+    if sink.device != buf.device or sink.numel() < 1:
+        raise ValueError("read_probe: sink must hold one int32 on the buffer's GPU")
+    st = _launch(lib.w4a16_read_probe, buf.get_device(), buf.data_ptr(), nbytes, sink.data_ptr())
+    _lib.check(st, "w4a16_read_probe")
+    return sink

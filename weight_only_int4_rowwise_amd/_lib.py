@@ -38,6 +38,7 @@ EXPORTS = (
     "w4a16_zp_geglu_linear",
     "w4a16_zp_linear_prepacked",
     "w4a16_zp_geglu_linear_prepacked",
+    "w4a16_read_probe",
 )
 
 ABI_VERSION = 1
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
                "w4a16_zp_geglu_linear_prepacked"):
         getattr(lib, fn).argtypes = [P, I, I, P, P, P, I, P, P, P]
         getattr(lib, fn).restype = ctypes.c_int
+    lib.w4a16_read_probe.argtypes = [P, I, P, P]
+    lib.w4a16_read_probe.restype = ctypes.c_int
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_last_error.argtypes = []

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_w8.hip", "decode_zp.hip", "prefill.hip",
-           "prepack.hip"]
+           "prepack.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

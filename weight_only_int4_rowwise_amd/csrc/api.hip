@@ -26,6 +26,7 @@ int64_t prepacked_bytes(int64_t n, int64_t k);
 hipError_t launch_prepack(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
 int64_t prepacked_bytes_int8(int64_t n, int64_t k);
 hipError_t launch_prepack_int8(const void *src, int64_t n, int64_t k, void *dst, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, int64_t bytes, void *sink, hipStream_t stream);
 }  // namespace w4a16
 
 namespace {
@@ -332,6 +333,19 @@ w4a16_status w4a16_zp_geglu_linear_prepacked(const void *x_fp16, int64_t m, int6
         return W4A16_ERR_SHAPE;
     return run_linear(x_fp16, m, k, q_prepacked, scales_fp16, f, bias_fp16, y_fp16, true, true, 4,
                       stream, zeros_u8, true);
+}
+
+w4a16_status w4a16_read_probe(const void *src, int64_t bytes, void *sink_u32, void *stream)
+{
+    if (bytes < 0 || bytes % 1024 != 0 || bytes > (int64_t(1) << 40))
+        return W4A16_ERR_SHAPE;
+    if (bytes == 0)
+        return W4A16_OK;
+    if (!src || !sink_u32)
+        return W4A16_ERR_NULL;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink_u32) & 3u) != 0)
+        return W4A16_ERR_ALIGN;
+    return from_hip(w4a16::launch_read_probe(src, bytes, sink_u32, static_cast<hipStream_t>(stream)));
 }
 
 const char *w4a16_status_string(int status)
