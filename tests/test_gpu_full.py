@@ -122,6 +122,22 @@ def test_geglu_decode_full(ffn, m):
     print(f"GeGLU up M={m}: max err/bound {r:.4f}")
 
 
+def test_down_prefill_m256_sampled(ffn):
+    """FFN-down 12288 x 32768 at m = 256 runs 192-row x 64-token tiles with
+    the reduction split over two halves of a 512-thread workgroup: one token
+    in every 64-token tile and two columns in every 192-row tile."""
+    _, (q, s, p_ref, s_ref), _, _ = ffn
+    m = 256
+    x = synth.activations(m, synth.FFN, synth.generator(11, DEV), DEV)
+    announce("FFN-down prefill", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(m, q.shape[0], 64, 192, 12)
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"FFN-down prefill M={m}")
+    print(f"FFN-down prefill M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 @pytest.mark.parametrize("m", [1, 16])
 def test_down_decode_full(ffn, m):
     _, (q, s, p_ref, s_ref), _, x_down = ffn
@@ -210,9 +226,10 @@ def test_prefill_attn_out_sampled(prefill_data):
 
 
 def test_prefill_attn_out_m512_sampled(prefill_data):
-    """m = 512 runs the small-grid tiles (192 rows x 64 tokens) on the
-    attention-out weight: one token in every 64-token tile and two columns
-    in every 192-row tile."""
+    """m = 512 on the attention-out weight runs 192-row x 128-token tiles
+    (one per CU) with the reduction split over two halves of a 512-thread
+    workgroup: one token in every 64-token block and two columns in every
+    192-row tile."""
     (q, s, p_ref, s_ref), _, x = prefill_data
     x5 = x[:512].contiguous()
     announce("prefill attn-out", tuple(x5.shape))

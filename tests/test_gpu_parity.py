@@ -411,6 +411,29 @@ def test_prefill_64_token_tiles(geglu):
         check_linear(x, q, s, p_ref, s_ref, f"prefill 64-token tiles {m}x{n}x{k}", bias)
 
 
+@pytest.mark.parametrize("k", [8320, 8224])
+def test_prefill_split_reduction(k):
+    """A small grid with a long reduction (3072 rows, m = 300: 80 tiles of
+    192 rows x 64 tokens on a 256-CU MI355X) splits the reduction over two
+    halves of a 512-thread workgroup: an odd number of 128-wide steps
+    (k = 8320), and a ragged last step (k = 8224); bias; both layouts
+    bit-identical; power-of-two scales with integer activations bit-exact."""
+    g = synth.generator(2400 + k)
+    m, n = 300, 3072
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill split reduction n={n} k={k}")
+    check_linear(x, q, s, p_ref, s_ref, f"prefill split reduction {m}x{n}x{k} bias", bias)
+    xd, bd = x.to(DEV), bias.to(DEV)
+    y0 = w4.w4a16_linear(xd, q, s, bd)
+    y1 = w4.w4a16_linear_prepacked(xd, w4.w4a16_prepack(q), s, bd)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(y1), bits(y0), f"prefill split reduction prepacked vs row-major k={k}")
+    if k == 8320:
+        _pow2_case(m, n, k, 2500)
+
+
 @pytest.mark.parametrize("geglu,m,n,k", [(False, 2000, 12280, 160), (False, 2000, 16380, 256),
                                          (True, 2000, 2 * 4080, 160)])
 def test_prefill_large_grids(geglu, m, n, k):

@@ -209,8 +209,10 @@ def test_zp_geglu_every_launch_class(f, k):
         check_geglu(synth.activations(m, k, g), qsz, f"geglu class {m}x{f}x{k} bias", bias)
 
 
-@pytest.mark.parametrize("m,n,k", [(200, 1000, 1120), (520, 2000, 256), (2000, 12280, 160)])
+@pytest.mark.parametrize("m,n,k", [(200, 1000, 1120), (520, 2000, 256), (2000, 12280, 160), (300, 3072, 8320)])
 def test_zp_prefill_shapes(m, n, k):
+    """Prefill tile shapes with zero points; 300 x 3072 x 8320 splits the
+    reduction over two halves of a 512-thread workgroup (odd step count)."""
     g = synth.generator(2500 + m + n)
     w = synth.weight(n, k, g, "t4")
     qsz = quantize_both(w, f"prefill {n}x{k}")

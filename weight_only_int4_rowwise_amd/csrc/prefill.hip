@@ -33,6 +33,14 @@
 //  * INT8 codes (the W8A16 variant, one byte per code) take two 16-byte
 //    weight loads per lane and row group per step and dequantize with
 //    dequant8_i8; everything else is shared.
+//  * KH = 2 splits the reduction inside the workgroup for grids of about
+//    one tile per CU or fewer: 512 threads, the first four wavefronts take
+//    the even 128-wide steps and the other four the odd ones, each group
+//    with its own activation tiles; at the end the second group's partial
+//    sums pass through LDS and the first group adds them (a fixed order,
+//    so results are deterministic) before its epilogue.  Twice the
+//    wavefronts per tile without smaller tiles, so each weight is still
+//    dequantized once per 64 or 128 tokens.
 #include "common.hpp"
 
 namespace w4a16 {
@@ -41,8 +49,8 @@ constexpr int kPBK = 128;                 // reduction step
 constexpr int kPRowBytes = 2 * kPBK;      // bytes of one token row per step
 constexpr int kPThreads = 256;
 
-template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED, int CB, bool ZP>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *__restrict__ x,
+template <int WN, int WT, bool EVEN, bool GEGLU, bool TILED, int CB, bool ZP, int KH>
+__global__ __launch_bounds__(kPThreads * KH, KH == 1 ? 2 : 1) void prefill_kernel(const uint16_t *__restrict__ x,
                                                             int64_t m, int64_t k,
                                                             const uint8_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
@@ -61,11 +69,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     constexpr int kStepBytes = BM * kPRowBytes;       // activation tile of one step
     constexpr int XC = kStepBytes / (4 * 1024);       // 1 KB DMA loads per wave per step
     static_assert(XC * 4 * 1024 == kStepBytes, "activation tile must split into 1 KB loads");
-    __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kStepBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[KH][2][kStepBytes];
 
     const int lane = threadIdx.x % kWave;
     // uniform: the DMA destinations and row offsets stay in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    static_assert(KH == 1 || KH == 2, "one or two reduction parts");
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kh = wave_all / 4;                      // reduction part: steps kh, kh + KH, ...
+    const int wave = wave_all % 4;                    // row slot of the tile
+    // steps per reduction part; a part's step past the end reads zeros
+    const int64_t nls = (((k + kPBK - 1) / kPBK) + KH - 1) / KH;
     const int r16 = lane % 16;
     const int g = lane / 16;
 
@@ -126,19 +139,21 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
 
     // Offsets below 2^31 plus kOutOfRange stay below 2^32 and out of range,
     // so a step past the end reads zeros.
-    auto load_x = [&](int64_t s, int buf) {
+    auto load_x = [&](int64_t ls, int buf) {
+        const int64_t s = ls * KH + kh;
         const uint32_t step = s < nsteps ? (uint32_t)s * kPRowBytes : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             uint32_t off = xbase[i] + step;
             if (!EVEN && (uint32_t)s * kPBK + xcol[i] >= k32)
                 off = kOutOfRange;
-            buf_load16_lds(xrs, off, &xs[buf][1024 * (XC * wave + i)]);
+            buf_load16_lds(xrs, off, &xs[kh][buf][1024 * (XC * wave + i)]);
         }
     };
     // INT8 codes take two 16-byte loads per row group: the lane's next 16
     // bytes (row-major) or the tile's second KB (prepacked).
-    auto load_w = [&](int64_t s, u32x4(&wd)[WN][WP]) {
+    auto load_w = [&](int64_t ls, u32x4(&wd)[WN][WP]) {
+        const int64_t s = ls * KH + kh;
         const uint32_t u = (uint32_t)s * kPBK;
         const uint32_t step = s < nsteps ? (TILED ? (uint32_t)s * 1024u * WP : u * CB / 8) : kOutOfRange;
 #pragma unroll
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
 #pragma unroll
             for (int b = 0; b < WT; ++b) {
                 const half8 bx = as_half8(*reinterpret_cast<const u32x4 *>(
-                    &xs[buf][rdoff[t] + 16 * kPRowBytes * b]));
+                    &xs[kh][buf][rdoff[t] + 16 * kPRowBytes * b]));
 #pragma unroll
                 for (int j = 0; j < WN; ++j)
                     acc[j][b] = mfma16x16x32(a[j], bx, acc[j][b]);
@@ -206,7 +221,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
         __builtin_amdgcn_sched_barrier(0);
         compute(0, wa);
         publish();
-        if (++s >= nsteps)
+        if (++s >= nls)
             break;
         load_x(s + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -214,8 +229,36 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
         __builtin_amdgcn_sched_barrier(0);
         compute(1, wb);
         publish();
-        if (++s >= nsteps)
+        if (++s >= nls)
             break;
+    }
+    if constexpr (KH > 1) {
+        // partial sums of reduction parts 1..KH-1 -> LDS (no wave reads the
+        // activation tiles after the last barrier); part 0 adds them in order
+        constexpr int kSlot = WN * WT * 4 * kWave;        // floats per wave
+        static_assert((KH - 1) * 4 * kSlot * 4 <= (int)sizeof(xs), "partials fit the tiles' LDS");
+        float *red = reinterpret_cast<float *>(&xs[0][0][0]);
+        if (kh > 0) {
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+#pragma unroll
+                for (int b = 0; b < WT; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[((kh - 1) * 4 + wave) * kSlot + ((j * WT + b) * kWave + lane) * 4 + i] = acc[j][b][i];
+        }
+        __syncthreads();
+        if (kh > 0)
+            return;
+#pragma unroll
+        for (int q = 1; q < KH; ++q)
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+#pragma unroll
+                for (int b = 0; b < WT; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[j][b][i] += red[((q - 1) * 4 + wave) * kSlot + ((j * WT + b) * kWave + lane) * 4 + i];
     }
 
     // epilogue: lane holds D[4 g + i][r16] of tile (j, b), i.e. outputs
@@ -267,7 +310,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(const uint16_t *_
     }
 }
 
-template <int WN, int WT, bool GEGLU, bool TILED, int CB, bool ZP>
+template <int WN, int WT, bool GEGLU, bool TILED, int CB, bool ZP, int KH = 1>
 static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const void *packed,
                                    const void *scales, int64_t n_out, const void *bias,
                                    const void *zeros, void *y, hipStream_t stream)
@@ -285,8 +328,8 @@ static hipError_t launch_prefill_t(const void *x, int64_t m, int64_t k, const vo
     const uint8_t *zp = static_cast<const uint8_t *>(zeros);
     uint16_t *yp = static_cast<uint16_t *>(y);
 #define W4_PREFILL(EV)                                                                            \
-    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED, CB, ZP>), dim3((unsigned)grid),  \
-                       dim3(kPThreads), 0, stream, xp, m, k, pp, sp, n_out, bp, zp, yp, (int)tiles_m)
+    hipLaunchKernelGGL((prefill_kernel<WN, WT, EV, GEGLU, TILED, CB, ZP, KH>), dim3((unsigned)grid), \
+                       dim3(kPThreads * KH), 0, stream, xp, m, k, pp, sp, n_out, bp, zp, yp, (int)tiles_m)
     if (k % kPBK == 0)
         W4_PREFILL(true);
     else
@@ -329,6 +372,15 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //    against 467 us; QKV 36864 x 12288 at m = 256: 207 against 282 us);
     //    a grid that fills one wave exactly keeps the large tile (plain
     //    FFN-up 65536 x 12288 at m = 256: 331 against 371 us);
+    //    With k >= 8192, a plain grid of about one 192 x 128 tile per CU
+    //    (7/8 to 1) takes those tiles with the reduction split over two
+    //    halves of a 512-thread workgroup (attention-out 12288 x 12288 at
+    //    m = 512: 131.5-131.8 against 140.7-145.4 us; FFN-down at m = 512:
+    //    334-337 against 365-366 us), and one of at most 1.5 192 x 64 tiles
+    //    per CU takes the small tiles split the same way (attention-out at
+    //    m = 256: 75.3-75.5 against 88.0-88.3 us; FFN-down at m = 256:
+    //    198-202 against 224 us; attention-out at m = 384: 117.7 against
+    //    121.3 us); larger grids gain nothing from the split;
     //  * larger plain grids keep 128-token tiles unless 64-token tiles fill
     //    the last wave of workgroups much better (k <= 16384) and the
     //    128-token grid's last wave would leave at least half the CUs idle
@@ -366,8 +418,18 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     } else {
         const int64_t slots = 2 * cus;
         const double fill8 = wave_fill(g48, slots);
-        if (4 * g48 <= 9 * cus && fill8 < 0.9)
+        if (4 * g48 <= 9 * cus && fill8 < 0.9) {
+            // small grids; with a long reduction and about one 192-row tile
+            // per CU or fewer, split the reduction over two halves of a
+            // 512-thread workgroup instead of shrinking the tiles further
+            const int64_t tn3 = (n_out + 191) / 192;
+            const int64_t g38 = tn3 * ((m + 127) / 128), g34 = tn3 * ((m + 63) / 64);
+            if (k >= 8192 && 8 * g38 >= 7 * cus && g38 <= cus)
+                return launch_prefill_t<3, 8, GEGLU, TILED, CB, ZP, 2>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+            if (k >= 8192 && 2 * g34 <= 3 * cus)
+                return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP, 2>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
             return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        }
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
         const int64_t last = g48 % slots;             // workgroups of a partial last wave
         if (k <= 16384 && fill4 > fill8 + 0.1 && ((last > 0 && 2 * last <= cus) || k < 4096))
