@@ -81,6 +81,23 @@ def test_qkv_two_decode_launches_sampled(qkv):
     print(f"QKV M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
+def test_qkv_m128_sampled(qkv):
+    """QKV at m = 128 runs the GEMM (192-row x 64-token tiles, reduction
+    split over two halves of the workgroup) rather than two decode
+    launches: one token in every 16-token block and two columns in every
+    192-row tile, against the oracle."""
+    q, s, p_ref, s_ref, _ = qkv
+    m = 128
+    x = synth.activations(m, synth.HIDDEN, synth.generator(13, DEV), DEV)
+    announce("QKV m=128 GEMM", m)
+    y = w4.w4a16_linear(x, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(m, q.shape[0], 16, 192, 14)
+    y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
+    print(f"QKV M={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 def test_qkv_prefill_m1024_sampled(qkv):
     """QKV at m = 1024 runs 256-row x 64-token tiles (the 128-token grid
     would leave half the CUs idle in its last wave): one token in every

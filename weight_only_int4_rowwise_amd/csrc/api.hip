@@ -85,6 +85,19 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
     return W4A16_OK;
 }
 
+// 64 < m <= 128 runs the decode kernel twice (next function), except near
+// m = 128 on large INT4 weights with a long reduction, where the GEMM's
+// split-reduction tiles are faster (m = 128: QKV 36864 x 12288 124 against
+// 129 us, attention-out 12288 x 12288 65.6 against 69.9 us, FFN-down
+// 12288 x 32768 160 against 168 us, GeGLU FFN-up 65536 x 12288 202 against
+// 209 us); below m = 112 the two decode launches win on every GLM-130B
+// shape, and at any m on short reductions (k = 3072) and thin weights
+// (4608 rows).
+bool gemm_beats_two_decodes(int64_t m, int64_t k, int64_t rows, int cb)
+{
+    return cb == 4 && m >= 120 && k >= 8192 && rows >= 8192;
+}
+
 // zeros: per-row zero points of the zero-point INT4 variant, or NULL.
 w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, const void *s,
                         int64_t n_out, const void *bias, void *y, bool geglu, bool tiled, int cb,
@@ -107,7 +120,7 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
     hipError_t e;
     if (m <= kDecodeMaxM) {
         e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, zeros, y, geglu, tiled, cb, hs);
-    } else if (m <= 2 * kDecodeMaxM) {
+    } else if (m <= 2 * kDecodeMaxM && !gemm_beats_two_decodes(m, k, rows, cb)) {
         // 64 < m <= 128: the first 64 tokens, then the rest, each through
         // the decode kernel.  The weights stream twice, but every CU stays
         // busy, where the GEMM's tiles leave most of the chip idle at this
