@@ -462,6 +462,27 @@ def test_prefill_large_grids(geglu, m, n, k):
     assert_bits_equal(bits(y1), bits(y0), f"prefill large grid prepacked vs row-major {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m", [1000, 1060])
+def test_prefill_geglu_tile_choice(m):
+    """f = 4096 on a 256-CU MI355X: at m = 1000 one 128 x 128 tile per CU,
+    so 64-output tiles, 128 tokens wide (their grid gives two per CU); at
+    m = 1060 the 128-token tiles would pad half a tile more than 64-token
+    ones and those fit one wave at three per CU, so 128 outputs x 64
+    tokens.  Ragged tokens, short k, bias, both layouts bit-identical."""
+    g = synth.generator(2700 + m)
+    f, k = 4096, 160
+    w = synth.weight(2 * f, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((2 * f,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill geglu tiles f={f}")
+    check_geglu(x, q, s, p_ref, s_ref, f"prefill geglu tiles {m}x{f}x{k} bias", bias)
+    xd, bd = x.to(DEV), bias.to(DEV)
+    y0 = w4.w4a16_geglu_linear(xd, q, s, bd)
+    y1 = w4.w4a16_geglu_linear_prepacked(xd, w4.w4a16_prepack(q), s, bd)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(y1), bits(y0), f"prefill geglu tiles prepacked vs row-major m={m}")
+
+
 @pytest.mark.parametrize("m,f,k", [(65, 100, 256), (200, 300, 1024), (257, 64, 64)])
 def test_prefill_geglu_small(m, f, k):
     g = synth.generator(900 + m)

@@ -390,7 +390,14 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //    attention-out 12288 x 12288 at m = 2048 runs 470-476 us on
     //    128-token tiles against 484-486 us on 64-token tiles, QKV at
     //    m = 1536 1037-1040 against 1089-1091 us;
-    //  * larger GeGLU grids take 128-token tiles.
+    //  * GeGLU grids of at most one 128 x 128 tile per CU take 64-output
+    //    tiles, 128 tokens wide when that grid still gives two per CU (FFN-up
+    //    65536 x 12288 at m = 128: 188.9 against 200.0 us for 64 x 64 tiles;
+    //    its 4-way shard 16384 x 12288 at m = 512: 177.4 against 187.6 us);
+    //  * larger GeGLU grids take 128 x 128 tiles, or 128 outputs x 64 tokens
+    //    where 128-token tiles would pad half a tile more and the 64-token
+    //    grid fits one wave at three per CU (FFN-up at m = 192: 268.6
+    //    against 326.4 us); the split reduction gains nothing for GeGLU.
     //  * INT8 codes need a second weight register set per row group, so
     //    their large tiles keep 128 tokens with one row group fewer per
     //    wave: 192 rows (GeGLU: 64 outputs) x 128 tokens, 188-204 VGPRs
@@ -412,8 +419,17 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
             return launch_prefill_t<3, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
         }
     } else if constexpr (GEGLU) {
-        if (g48 <= cus)
+        const int64_t tm8 = (m + 127) / 128, tm4 = (m + 63) / 64;
+        if (g48 <= cus) {
+            // 64-output tiles; 128 tokens when that grid still gives two per CU
+            if (((n_out + 63) / 64) * tm8 >= 2 * cus)
+                return launch_prefill_t<2, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
             return launch_prefill_t<2, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+        }
+        // 64-token tiles when 128-token ones would pad half a tile more and
+        // the 64-token grid fits one wave at three per CU
+        if (tm8 * 128 - tm4 * 64 >= 64 && tiles_n * tm4 <= 3 * cus)
+            return launch_prefill_t<4, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
         return launch_prefill_t<4, 8, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
     } else {
         const int64_t slots = 2 * cus;
