@@ -396,8 +396,8 @@ def test_prefill_one_hot_and_pow2_bit_exact(m):
 @pytest.mark.parametrize("geglu", [False, True])
 def test_prefill_64_token_tiles(geglu):
     """A small grid (13 output tiles x 4 token tiles of the largest shape)
-    takes 64-token tiles (192 rows; GeGLU 64 outputs); ragged rows, tokens
-    and k."""
+    takes 64-token tiles (128 rows with the reduction split; GeGLU 64
+    outputs); ragged rows, tokens and k."""
     g = synth.generator(1800 + geglu)
     m, k = 500, 160
     n = 3328 - 6 if not geglu else 2 * 1661
@@ -413,9 +413,9 @@ def test_prefill_64_token_tiles(geglu):
 
 @pytest.mark.parametrize("k", [8320, 8224])
 def test_prefill_split_reduction(k):
-    """A small grid with a long reduction (3072 rows, m = 300: 80 tiles of
-    192 rows x 64 tokens on a 256-CU MI355X) splits the reduction over two
-    halves of a 512-thread workgroup: an odd number of 128-wide steps
+    """A small grid with a long reduction (3072 rows, m = 300, on a 256-CU
+    MI355X) takes 128-row x 64-token tiles with the reduction split over
+    two halves of a 512-thread workgroup: an odd number of 128-wide steps
     (k = 8320), and a ragged last step (k = 8224); bias; both layouts
     bit-identical; power-of-two scales with integer activations bit-exact."""
     g = synth.generator(2400 + k)
@@ -432,6 +432,26 @@ def test_prefill_split_reduction(k):
     assert_bits_equal(bits(y1), bits(y0), f"prefill split reduction prepacked vs row-major k={k}")
     if k == 8320:
         _pow2_case(m, n, k, 2500)
+
+
+@pytest.mark.parametrize("m,n", [(199, 32832), (129, 10944), (129, 32832), (325, 32832), (129, 256), (2053, 1024)])
+def test_prefill_small_grid_shapes(m, n):
+    """Small plain grids take the tile shape of least modelled time; on a
+    256-CU MI355X these (m, n) pick 192 x 64, split 192 x 64, 256 x 64,
+    256 x 128, split 128 x 64 and split 192 x 64 tiles.  Short ragged k
+    (two steps, the second partial), bias, both layouts bit-identical."""
+    g = synth.generator(2800 + m + n)
+    k = 160
+    w = synth.weight(n, k, g, "t4")
+    x = synth.activations(m, k, g)
+    bias = synth.normal_fp16((n,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"prefill small grid n={n}")
+    check_linear(x, q, s, p_ref, s_ref, f"prefill small grid {m}x{n}x{k} bias", bias)
+    xd, bd = x.to(DEV), bias.to(DEV)
+    y0 = w4.w4a16_linear(xd, q, s, bd)
+    y1 = w4.w4a16_linear_prepacked(xd, w4.w4a16_prepack(q), s, bd)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(y1), bits(y0), f"prefill small grid prepacked vs row-major {m}x{n}")
 
 
 @pytest.mark.parametrize("geglu,m,n,k", [(False, 2000, 12280, 160), (False, 2000, 16380, 256),

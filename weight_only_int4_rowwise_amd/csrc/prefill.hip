@@ -43,6 +43,8 @@
 //    dequantized once per 64 or 128 tokens.
 #include "common.hpp"
 
+#include <math.h>
+
 namespace w4a16 {
 
 constexpr int kPBK = 128;                 // reduction step
@@ -356,6 +358,49 @@ static int64_t compute_units()
     return cus;
 }
 
+// Small plain grids: the tile shape (and reduction split) with the least
+// modelled time.  Shape i has tiles of 64 WN rows x 16 WT tokens, `slots`
+// workgroups resident per CU (from its registers and LDS) and a relative
+// throughput `rate`.  A grid of g tiles runs full = g / (slots cus) rounds
+// of `slots` concurrent tiles per CU and a last round of r = ceil(rem /
+// cus); j concurrent tiles on a CU take j^0.7 single-tile times (a CU's
+// throughput grows as j^0.3 with more resident tiles), so the modelled time
+// is (full slots^0.7 + r^0.7) 64 WN 16 WT / rate.  The rates and the
+// exponent were fitted to 166 timings of every shape at the GLM-130B widths
+// and their 2-, 4- and 8-way shards (n = 4608 ... 65536, k = 3072 ... 32768,
+// m = 129 ... 1024, every grid of this branch): the chosen shape came within
+// 0.35% of the fastest on average, where fixed thresholds were 4.6% off
+// (and up to 21%: the 4-way QKV shard 9216 x 12288 at m = 129 ... 192 runs
+// 52 us on split 128 x 64 tiles against 66 us on 192 x 64 ones).
+struct SmallTile {
+    int wn, wt, kh, slots;
+    double rate;
+};
+// (192 x 128 tiles were fitted too, rate 0.934, but are never the least
+// time on this branch; the split 192 x 128 tiles are chosen before it.)
+constexpr SmallTile kSmallTiles[] = {{3, 4, 1, 4, 0.809}, {4, 4, 1, 3, 0.899}, {4, 8, 1, 2, 1.0},
+                                     {3, 4, 2, 2, 0.906}, {2, 4, 2, 2, 0.835}};
+
+static int small_grid_tile(int64_t m, int64_t n_out, int64_t cus)
+{
+    int best = 0;
+    double best_t = 0.0;
+    for (int i = 0; i < (int)(sizeof kSmallTiles / sizeof kSmallTiles[0]); ++i) {
+        const SmallTile &t = kSmallTiles[i];
+        const int64_t rows = 64 * t.wn, tokens = 16 * t.wt;
+        const int64_t g = ((n_out + rows - 1) / rows) * ((m + tokens - 1) / tokens);
+        const int64_t full = g / (t.slots * cus), rem = g - full * t.slots * cus;
+        const int64_t r = (rem + cus - 1) / cus;
+        const double units = (double)full * pow((double)t.slots, 0.7) + (r ? pow((double)r, 0.7) : 0.0);
+        const double time = units * (double)(rows * tokens) / t.rate;
+        if (i == 0 || time < best_t) {
+            best = i;
+            best_t = time;
+        }
+    }
+    return best;
+}
+
 template <bool GEGLU, bool TILED, int CB, bool ZP>
 static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, const void *packed,
                                         const void *scales, int64_t n_out, const void *bias,
@@ -364,23 +409,16 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     // Tile shape from the grid of the largest tile (4 x 16 x 4 rows x 128
     // tokens; GeGLU 128 outputs x 128 tokens), measured at the GLM-130B
     // widths for m = 128 ... 2048:
-    //  * a grid of at most about two such tiles per CU that does not fill
-    //    a whole wave of workgroups (two per CU) leaves CUs idle or thinly
-    //    used: the 192-row x 64-token tile (GeGLU: 64 outputs x 64 tokens,
-    //    at one large tile per CU or fewer) runs 4 workgroups per CU and
-    //    gives the most of them (FFN-down 12288 x 32768 at m = 256: 235
-    //    against 467 us; QKV 36864 x 12288 at m = 256: 207 against 282 us);
-    //    a grid that fills one wave exactly keeps the large tile (plain
-    //    FFN-up 65536 x 12288 at m = 256: 331 against 371 us);
-    //    With k >= 8192, a plain grid of about one 192 x 128 tile per CU
-    //    (7/8 to 1) takes those tiles with the reduction split over two
+    //  * a plain grid of at most about two such tiles per CU that does not
+    //    fill a whole wave of workgroups (two per CU) leaves CUs idle or
+    //    thinly used: with k >= 8192 and about one 192 x 128 tile per CU
+    //    (7/8 to 1) it takes those tiles with the reduction split over two
     //    halves of a 512-thread workgroup (attention-out 12288 x 12288 at
-    //    m = 512: 131.5-131.8 against 140.7-145.4 us; FFN-down at m = 512:
-    //    334-337 against 365-366 us), and one of at most 1.5 192 x 64 tiles
-    //    per CU takes the small tiles split the same way (attention-out at
-    //    m = 256: 75.3-75.5 against 88.0-88.3 us; FFN-down at m = 256:
-    //    198-202 against 224 us; attention-out at m = 384: 117.7 against
-    //    121.3 us); larger grids gain nothing from the split;
+    //    m = 512: 131.5-131.8 against 136.0-136.2 us split 192 x 64;
+    //    FFN-down 12288 x 32768 at m = 512: 334-342 against 360-376 us),
+    //    otherwise the shape of least modelled time (small_grid_tile:
+    //    192 or 256 rows x 64 or 128 tokens, or 192 or 128 rows x 64 tokens
+    //    with the reduction split);
     //  * larger plain grids keep 128-token tiles unless 64-token tiles fill
     //    the last wave of workgroups much better (k <= 16384) and the
     //    128-token grid's last wave would leave at least half the CUs idle
@@ -435,16 +473,25 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
         const int64_t slots = 2 * cus;
         const double fill8 = wave_fill(g48, slots);
         if (4 * g48 <= 9 * cus && fill8 < 0.9) {
-            // small grids; with a long reduction and about one 192-row tile
-            // per CU or fewer, split the reduction over two halves of a
-            // 512-thread workgroup instead of shrinking the tiles further
-            const int64_t tn3 = (n_out + 191) / 192;
-            const int64_t g38 = tn3 * ((m + 127) / 128), g34 = tn3 * ((m + 63) / 64);
+            // small grids: about one 192 x 128 tile per CU with a long
+            // reduction takes those tiles with the reduction split; other
+            // small grids take the shape of least modelled time
+            const int64_t g38 = ((n_out + 191) / 192) * ((m + 127) / 128);
             if (k >= 8192 && 8 * g38 >= 7 * cus && g38 <= cus)
                 return launch_prefill_t<3, 8, GEGLU, TILED, CB, ZP, 2>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
-            if (k >= 8192 && 2 * g34 <= 3 * cus)
-                return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP, 2>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
-            return launch_prefill_t<3, 4, GEGLU, TILED, CB, ZP>(x, m, k, packed, scales, n_out, bias, zeros, y, stream);
+#define W4_SMALL(I, WN, WT, KH)                                                                    \
+    case I:                                                                                        \
+        return launch_prefill_t<WN, WT, GEGLU, TILED, CB, ZP, KH>(x, m, k, packed, scales, n_out, bias, \
+                                                                  zeros, y, stream)
+            switch (small_grid_tile(m, n_out, cus)) {
+                W4_SMALL(0, 3, 4, 1);
+                W4_SMALL(1, 4, 4, 1);
+                W4_SMALL(2, 4, 8, 1);
+                W4_SMALL(3, 3, 4, 2);
+                default:
+                W4_SMALL(4, 2, 4, 2);
+            }
+#undef W4_SMALL
         }
         const double fill4 = wave_fill(tiles_n * ((m + 63) / 64), slots);
         const int64_t last = g48 % slots;             // workgroups of a partial last wave
