@@ -213,13 +213,20 @@ def _print_pmc(dirs):
             print(f"    {c:32s} {mean:16.1f}   ({n} dispatches)")
 
 
-def trace_stats(d, name_part=""):
+def trace_stats(d, name_part="", by_grid=False):
     """Per-kernel call count, mean, median, min and max duration (us) of a
-    --kernel-trace run, for kernels whose name contains name_part."""
+    --kernel-trace run, for kernels whose name contains name_part; with
+    by_grid, per (kernel, workgroups per launch), which tells apart the
+    workloads that share one kernel."""
     per = defaultdict(list)
-    for name, s, e in summarize_trace(d):
+    rows = _csv_rows([d], "kernel_trace.csv")
+    for r in rows:
+        name = r["Kernel_Name"]
         if name_part in name:
-            per[name].append((e - s) / 1e3)
+            if by_grid:
+                wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+                name = f"{name} [{wgs} workgroups]"
+            per[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     out = OrderedDict()
     for name, v in per.items():
         v = sorted(v)
@@ -228,8 +235,8 @@ def trace_stats(d, name_part=""):
     return out
 
 
-def _print_trace(d, sequence=False):
-    for name, st in trace_stats(d).items():
+def _print_trace(d, sequence=False, by_grid=False):
+    for name, st in trace_stats(d, by_grid=by_grid).items():
         print(f"{st['calls']:6d} calls  mean {st['mean']:9.2f} us  median {st['median']:9.2f}  "
               f"min {st['min']:9.2f}  max {st['max']:9.2f}  {name}")
     if not sequence:
@@ -262,6 +269,7 @@ def main(argv=None):
     p = sub.add_parser("summarize-trace")
     p.add_argument("dir")
     p.add_argument("--sequence", action="store_true", help="also list every launch in order")
+    p.add_argument("--by-grid", action="store_true", help="one line per kernel and grid size")
     p = sub.add_parser("derived")
     p.add_argument("kernel_part")
     p.add_argument("dirs", nargs="+")
@@ -287,7 +295,7 @@ def main(argv=None):
         _print_pmc(a.dirs)
         return 0
     if a.mode == "summarize-trace":
-        _print_trace(a.dir, a.sequence)
+        _print_trace(a.dir, a.sequence, a.by_grid)
         return 0
 
     import torch
