@@ -529,8 +529,9 @@ def read_probe_table(torch, w4, dev):
 def intermediate_m(torch, w4, synth, dev, mats, g):
     """Batched decode between the decode and prefill configurations: QKV,
     attention-out and the fused GeGLU up-projection at m = 96 ... 384 tokens
-    (m = 96 runs the decode kernel twice, m = 128 and larger the prefill
-    GEMM), prepacked, with both the HBM and the MFMA fraction of each launch."""
+    (QKV and FFN-up at m = 96 run the decode kernel twice, attention-out at
+    m = 96 and every shape from m = 128 the prefill GEMM), prepacked, with
+    both the HBM and the MFMA fraction of each launch."""
     H = synth.HIDDEN
     out = {}
     for name, (rot, n_rows, k, geglu) in mats.items():

@@ -99,9 +99,13 @@ w4a16_status quantize_rowwise_int4(const void *w_fp16, int64_t n, int64_t k,
  *   y_fp16      out  fp16  [m][n]
  *
  * m <= 64 runs the memory-bound decode kernel, 64 < m <= 128 runs it twice
- * (tokens 0..63, then the rest), larger m runs the MFMA GEMM; 120 <= m <= 128
- * also runs the GEMM when k >= 8192 and n >= 8192 (2f for GeGLU), where it
- * is faster.  Results are deterministic (no atomics, fixed reduction order).
+ * (tokens 0..63, then the rest), larger m runs the MFMA GEMM.  INT4 calls
+ * also take the GEMM from a threshold between m = 65 and 120 where one GEMM
+ * launch is faster than two decode launches; it depends on the weight's
+ * rows (n, or 2f for GeGLU) and, for 8192 to 16383 plain rows, on k.  Plain
+ * weights of fewer than 8192 rows take it only with k >= 8192 (from
+ * m = 104), GeGLU weights of fewer than 12288 rows never.
+ * Results are deterministic (no atomics, fixed reduction order).
  */
 w4a16_status w4a16_linear(const void *x_fp16, int64_t m, int64_t k,
                           const void *q_packed, const void *scales_fp16, int64_t n,

@@ -258,6 +258,22 @@ def test_prefill_attn_out_m512_sampled(prefill_data):
     print(f"prefill attn-out m=512: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
+def test_attn_out_m96_gemm_sampled(prefill_data):
+    """m = 96 on the attention-out weight (12288 x 12288) runs one GEMM
+    launch rather than two decode launches (128-row x 64-token tiles, the
+    reduction split over two halves of the workgroup): one token in every
+    16-token block and two columns in every 128-row tile."""
+    (q, s, p_ref, s_ref), _, x = prefill_data
+    x96 = x[:96].contiguous()
+    announce("attn-out m=96 GEMM", tuple(x96.shape))
+    y = w4.w4a16_linear(x96, q, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(x96.shape[0], q.shape[0], 16, 128, 9)
+    y_ref, mag = oracle.linear_at(bits(x96), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "attn-out m=96")
+    print(f"attn-out m=96: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 def test_prefill_ffn_up_geglu_sampled(prefill_data):
     _, (q, s, p_ref, s_ref), x = prefill_data
     announce("prefill FFN-up GeGLU", tuple(x.shape))

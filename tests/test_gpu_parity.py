@@ -244,6 +244,39 @@ def test_decode_every_launch_class(n, k):
         assert_bits_equal(bits(y1), bits(y0), f"class prepacked vs row-major {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("geglu,rows,k,m_gemm", [
+    (False, 8192, 3072, 65),    # 8192-16383 rows, k < 4096
+    (False, 8192, 4096, 80),    # 8192-16383 rows, 4096 <= k < 8192
+    (False, 16384, 1024, 69),   # 16384-24575 rows
+    (True, 24576, 1024, 65),    # GeGLU, 24576-49151 rows of both halves
+])
+def test_gemm_threshold_in_two_launch_range(geglu, rows, k, m_gemm):
+    """64 < m <= 128: INT4 calls take one GEMM launch from a threshold m
+    set by the weight's rows and, for 8192-16383 rows, its reduction
+    length; below it, two decode launches.  At the threshold and one token
+    below it (where the result must also equal separate calls on tokens
+    0..63 and the rest, bit for bit), every output against the oracle."""
+    g = synth.generator(2400 + rows // 1024 + k // 256 + geglu)
+    w = synth.weight(rows, k, g, "t4")
+    bias = synth.normal_fp16((rows,), 0.5, g)
+    q, s, p_ref, s_ref = quantize_both(w, f"GEMM threshold rows={rows} k={k}")
+    check = check_geglu if geglu else check_linear
+    f = w4.w4a16_geglu_linear if geglu else w4.w4a16_linear
+    for m in (m_gemm - 1, m_gemm):
+        if m <= 64:
+            continue
+        x = synth.activations(m, k, g)
+        check(x, q, s, p_ref, s_ref, f"threshold geglu={geglu} rows={rows} k={k} m={m}", bias)
+        if m < m_gemm:
+            announce("below the GEMM threshold: split calls", m, rows, k, geglu)
+            xd, bd = x.to(DEV), bias.to(DEV)
+            y = f(xd, q, s, bd)
+            lo = f(xd[:64].contiguous(), q, s, bd)
+            hi = f(xd[64:].contiguous(), q, s, bd)
+            torch.cuda.synchronize()
+            assert_bits_equal(bits(y), np.concatenate([bits(lo), bits(hi)]), f"two launches vs split calls m={m}")
+
+
 @pytest.mark.parametrize("m", [65, 100, 128])
 def test_two_decode_launches(m):
     """64 < m <= 128 runs the decode kernel on tokens 0..63, then on the

@@ -85,17 +85,47 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
     return W4A16_OK;
 }
 
-// 64 < m <= 128 runs the decode kernel twice (next function), except near
-// m = 128 on large INT4 weights with a long reduction, where the GEMM's
-// split-reduction tiles are faster (m = 128: QKV 36864 x 12288 124 against
-// 129 us, attention-out 12288 x 12288 65.6 against 69.9 us, FFN-down
-// 12288 x 32768 160 against 168 us, GeGLU FFN-up 65536 x 12288 202 against
-// 209 us); below m = 112 the two decode launches win on every GLM-130B
-// shape, and at any m on short reductions (k = 3072) and thin weights
-// (4608 rows).
-bool gemm_beats_two_decodes(int64_t m, int64_t k, int64_t rows, int cb)
+// 64 < m <= 128 runs the decode kernel twice (next function), unless one
+// GEMM launch is faster: from the m this returns, by weight height in the
+// decode kernel's own bands (the second decode launch gets slower as m - 64
+// crosses its token classes, while the GEMM costs about the same anywhere in
+// 64 < m <= 128) and, for 8192 to 16383 rows, by reduction length.  Measured
+// on MI355X, prepacked INT4, two decode launches against one GEMM (us):
+//  * QKV 36864 x 12288 and plain 65536 x 12288: m = 112 118 / 126,
+//    m = 120 127 / 124 (FFN-up 191 / 196, 203 / 196);
+//  * 2-way QKV shard 18432 x 12288 (its M = 64 decode has 128 workgroups):
+//    m = 65 72.4 / 72.0, m = 72 73.6 / 68.9;
+//  * 8192 to 16383 rows: k >= 8192 (attention-out 12288 x 12288, FFN-down
+//    12288 x 32768 and its 2- and 4-way shards, 4-way QKV 9216 x 12288):
+//    m = 80 51.3 / 53.4, m = 88 55.7 / 51.9 (attention-out); 4096 <= k
+//    < 8192 (12288 x 6144, 12288 x 4096): m = 72 22.2 / 22.8, m = 80
+//    23.5 / 22.4; k < 4096 (12288 x 3072, 12288 x 1536): m = 65 13.8 /
+//    12.4 (k = 1536);
+//  * fewer rows with a long reduction (8-way QKV 4608 x 12288): m = 96
+//    47.5 / 50.3, m = 104 53.8 / 50.3;
+//  * GeGLU FFN-up 65536 x 12288: m = 112 191.5 / 192.0, m = 120 200.5 /
+//    192.5; its 2-way shard (32768 rows): m = 65 121.9 / 108.5; 4-way
+//    (16384 rows): m = 96 68.4 / 69.2, m = 104 78.0 / 71.2; 8-way (8192
+//    rows): two decode launches at every m (m = 128 63.1 / 66.4).
+// Shapes below these bands keep two decode launches.  INT8 codes always do:
+// their GEMM has no split-reduction tiles.
+static int64_t gemm_from_m(int64_t k, int64_t rows, bool geglu)
 {
-    return cb == 4 && m >= 120 && k >= 8192 && rows >= 8192;
+    const int64_t never = 2 * kDecodeMaxM + 1;
+    if (geglu)
+        return rows >= 49152 ? 120 : rows >= 24576 ? 65 : rows >= 12288 ? 104 : never;
+    if (rows >= 24576)
+        return 120;
+    if (rows >= 16384)
+        return 69;
+    if (rows >= 8192)
+        return k >= 8192 ? 88 : k >= 4096 ? 80 : 65;
+    return k >= 8192 ? 104 : never;
+}
+
+static bool gemm_beats_two_decodes(int64_t m, int64_t k, int64_t rows, bool geglu, int cb)
+{
+    return cb == 4 && m >= gemm_from_m(k, rows, geglu);
 }
 
 // zeros: per-row zero points of the zero-point INT4 variant, or NULL.
@@ -120,7 +150,7 @@ w4a16_status run_linear(const void *x, int64_t m, int64_t k, const void *q, cons
     hipError_t e;
     if (m <= kDecodeMaxM) {
         e = w4a16::launch_decode(x, (int)m, k, q, s, n_out, bias, zeros, y, geglu, tiled, cb, hs);
-    } else if (m <= 2 * kDecodeMaxM && !gemm_beats_two_decodes(m, k, rows, cb)) {
+    } else if (m <= 2 * kDecodeMaxM && !gemm_beats_two_decodes(m, k, rows, geglu, cb)) {
         // 64 < m <= 128: the first 64 tokens, then the rest, each through
         // the decode kernel.  The weights stream twice, but every CU stays
         // busy, where the GEMM's tiles leave most of the chip idle at this
