@@ -514,17 +514,12 @@ void launch_decode_e(const void *x, int m, int64_t k, const void *packed, const 
 // (k <= 4096) wants a short round (128 or 256 columns per K-part), or the
 // ring never fills; a long one (the 32768-column FFN-down at m <= 8) wants
 // three row groups per wavefront and eight K-parts (36.8 against 38.7 us).
-// At m <= 8, 12288 to 16383 rows with 4096 <= k < 24576 take the same row
-// groups and K-parts with one 128-index piece per chunk, a grid of one
-// 48-row workgroup per CU for 12288 rows (2-way shard FFN-down
-// 12288 x 16384: 20.5 against 21.4-23.0 us; 2-way attention-out
-// 12288 x 6144: 9.7 against 10.2 us; the full 12288 x 12288 attention-out
-// ties at 15.9 us), and the 2-way QKV shard (16384 to 24575 rows) takes
-// two row sets of three groups (18432 x 12288: 22.3-22.9 against
-// 23.8-24.2 us).  More token blocks want more row groups per wavefront
-// (each activation operand feeds more MFMAs).  At m > 48 tall weights keep
-// three weight register sets in flight (D = 3): the round there is long
-// enough that two sets leave the wave waiting on the loads.
+// At m <= 8 the 2-way QKV shard band (16384 to 24575 rows) takes two row
+// sets of three groups (18432 x 12288 on quantized normal weights:
+// 21.6-22.0 against 23.4-23.6 us).  More token blocks want more row groups
+// per wavefront (each activation operand feeds more MFMAs).  At m > 48 tall
+// weights keep three weight register sets in flight (D = 3): the round there
+// is long enough that two sets leave the wave waiting on the loads.
 template <bool GEGLU, bool TILED, bool ZP>
 hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *packed,
                                  const void *scales, int64_t n_out, const void *bias,
@@ -581,8 +576,7 @@ hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *pa
             : b == 2 ? W4_DEC(2, 2, 8, 2, 1, 8, 3)
             : b == 1 ? (k < 4096    ? W4_DEC(1, 1, 4, 2, 1, 8, 1)
                         : k >= 24576 ? W4_DEC(2, 1, 8, 2, 1, 8, 3)
-                        : rows >= 12288 ? W4_DEC(1, 1, 8, 2, 1, 8, 3)
-                                        : W4_DEC(4, 3, 12, 2, 1, 8, 1))
+                                     : W4_DEC(4, 3, 12, 2, 1, 8, 1))
                      : W4_DEC(2, 2, 8, 2, 1, 8, 1);
         else if (m <= 16)
             b == 4                  ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
