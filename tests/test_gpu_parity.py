@@ -247,7 +247,7 @@ def test_decode_every_launch_class(n, k):
 @pytest.mark.parametrize("geglu,rows,k,m_gemm", [
     (False, 8192, 3072, 65),    # 8192-16383 rows, k < 4096
     (False, 8192, 4096, 80),    # 8192-16383 rows, 4096 <= k < 8192
-    (False, 16384, 1024, 69),   # 16384-24575 rows
+    (False, 16384, 1024, 65),   # 16384-24575 rows
     (True, 24576, 1024, 65),    # GeGLU, 24576-49151 rows of both halves
 ])
 def test_gemm_threshold_in_two_launch_range(geglu, rows, k, m_gemm):

@@ -90,23 +90,25 @@ w4a16_status check_gemm_ptrs(const void *x, const void *q, const void *s, const 
 // decode kernel's own bands (the second decode launch gets slower as m - 64
 // crosses its token classes, while the GEMM costs about the same anywhere in
 // 64 < m <= 128) and, for 8192 to 16383 rows, by reduction length.  Measured
-// on MI355X, prepacked INT4, two decode launches against one GEMM (us):
-//  * QKV 36864 x 12288 and plain 65536 x 12288: m = 112 118 / 126,
-//    m = 120 127 / 124 (FFN-up 191 / 196, 203 / 196);
+// on MI355X on the codes of quantized normal weights, prepacked, two decode
+// launches against one GEMM launch (us):
+//  * QKV 36864 x 12288 and plain 65536 x 12288: m = 112 115.3 / 122.5,
+//    m = 120 125.5 / 122.9 (FFN-up 185.3 / 190.6, 195.5 / 190.7);
 //  * 2-way QKV shard 18432 x 12288 (its M = 64 decode has 128 workgroups):
-//    m = 65 72.4 / 72.0, m = 72 73.6 / 68.9;
+//    m = 65 76.0 / 71.5;
 //  * 8192 to 16383 rows: k >= 8192 (attention-out 12288 x 12288, FFN-down
 //    12288 x 32768 and its 2- and 4-way shards, 4-way QKV 9216 x 12288):
-//    m = 80 51.3 / 53.4, m = 88 55.7 / 51.9 (attention-out); 4096 <= k
-//    < 8192 (12288 x 6144, 12288 x 4096): m = 72 22.2 / 22.8, m = 80
-//    23.5 / 22.4; k < 4096 (12288 x 3072, 12288 x 1536): m = 65 13.8 /
+//    m = 80 52.1 / 53.2, m = 88 55.9 / 52.0 (attention-out); 4096 <= k
+//    < 8192 (12288 x 6144, 12288 x 4096): m = 72 22.4 / 22.7, m = 80
+//    23.4 / 22.7; k < 4096 (12288 x 3072, 12288 x 1536): m = 65 13.8 /
 //    12.4 (k = 1536);
 //  * fewer rows with a long reduction (8-way QKV 4608 x 12288): m = 96
-//    47.5 / 50.3, m = 104 53.8 / 50.3;
-//  * GeGLU FFN-up 65536 x 12288: m = 112 191.5 / 192.0, m = 120 200.5 /
-//    192.5; its 2-way shard (32768 rows): m = 65 121.9 / 108.5; 4-way
-//    (16384 rows): m = 96 68.4 / 69.2, m = 104 78.0 / 71.2; 8-way (8192
-//    rows): two decode launches at every m (m = 128 63.1 / 66.4).
+//    47.6 / 50.8, m = 104 53.8 / 50.6;
+//  * GeGLU FFN-up 65536 x 12288: m = 96 170.6 / 181.8, m = 104 to 112
+//    even, m = 120 195.1 / 186.9; its 2-way shard (32768 rows): m = 65
+//    119.9 / 103.9; 4-way (16384 rows): m = 96 67.8 / 68.8, m = 104 74.4 /
+//    69.0; 8-way (8192 rows): two decode launches at every m (m = 128
+//    62.1 / 66.1).
 // Shapes below these bands keep two decode launches.  INT8 codes always do:
 // their GEMM has no split-reduction tiles.
 static int64_t gemm_from_m(int64_t k, int64_t rows, bool geglu)
@@ -117,7 +119,7 @@ static int64_t gemm_from_m(int64_t k, int64_t rows, bool geglu)
     if (rows >= 24576)
         return 120;
     if (rows >= 16384)
-        return 69;
+        return 65;
     if (rows >= 8192)
         return k >= 8192 ? 88 : k >= 4096 ? 80 : 65;
     return k >= 8192 ? 104 : never;
