@@ -544,23 +544,25 @@ hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *pa
             : b    ? W4_DEC(2, 2, 8, 2, 1, 8, 2)
                    : W4_DEC(2, 1, 8, 2, 1, 8, 2);
         else if (m <= 16)
-            b == 3 ? W4_DEC(2, 8, 16, 2, 1, 16, 2)
-            : b    ? W4_DEC(2, 2, 8, 2, 1, 16, 2)
-                   : W4_DEC(2, 1, 8, 2, 1, 16, 2);
+            b == 3   ? W4_DEC(2, 8, 16, 2, 1, 16, 2)
+            : b == 2 ? W4_DEC(2, 4, 16, 2, 1, 16, 2)
+            : b == 1 ? W4_DEC(2, 2, 8, 2, 1, 16, 2)
+                     : W4_DEC(2, 1, 8, 2, 1, 16, 2);
         else if (m <= 32)
             b == 3   ? W4_DEC(1, 4, 8, 2, 2, 32, 4)
-            : b == 2 ? W4_DEC(2, 2, 4, 2, 2, 32, 4)
+            : b == 2 ? W4_DEC(1, 2, 8, 2, 2, 32, 4)
             : b == 1 ? W4_DEC(2, 2, 8, 2, 2, 32, 2)
                      : W4_DEC(2, 1, 4, 2, 2, 32, 2);
         else if (m <= 48)
             b == 3   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
-            : b == 2 ? W4_DEC(1, 2, 4, 2, 3, 48, 4)
+            : b == 2 ? W4_DEC(1, 4, 16, 2, 3, 48, 2)
             : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 4)
-                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
+                     : W4_DEC(1, 1, 4, 3, 3, 48, 2);
         else
-            b == 3 ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
-            : b    ? W4_DEC(2, 2, 4, 2, 4, 64, 2)
-                   : W4_DEC(1, 1, 4, 2, 4, 64, 2);
+            b == 3   ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
+            : b == 2 ? W4_DEC(1, 4, 8, 3, 4, 64, 2)
+            : b == 1 ? W4_DEC(2, 2, 4, 2, 4, 64, 2)
+                     : W4_DEC(1, 1, 4, 3, 4, 64, 2);
     } else {
         // Height bands: 4 from 49152 rows, 3 from 24576, 2 from 16384,
         // 1 from 8192, 0 below.
@@ -579,26 +581,31 @@ hipError_t launch_decode_layout4(const void *x, int m, int64_t k, const void *pa
                                      : W4_DEC(4, 3, 12, 2, 1, 8, 1))
                      : W4_DEC(2, 2, 8, 2, 1, 8, 1);
         else if (m <= 16)
-            b == 4                  ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
-            : b == 3                ? W4_DEC(2, 3, 12, 2, 1, 16, 3)
-            : b == 2 || (b == 1 && k < 4096) ? W4_DEC(1, 1, 4, 2, 1, 16, 3)
-            : b == 1                ? W4_DEC(2, 1, 8, 2, 1, 16, 3)
-                                    : W4_DEC(2, 2, 8, 2, 1, 16, 1);
+            b == 4   ? W4_DEC(2, 4, 4, 2, 1, 16, 2)
+            : b == 3 ? W4_DEC(2, 3, 12, 2, 1, 16, 3)
+            : b == 2 ? W4_DEC(1, 3, 12, 3, 1, 16, 2)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 3, 12, 2, 1, 16, 1) : W4_DEC(2, 1, 8, 2, 1, 16, 3))
+                     : W4_DEC(2, 1, 8, 2, 1, 16, 2);
         else if (m <= 32)
             b == 4   ? W4_DEC(1, 2, 4, 2, 2, 32, 4)
-            : b >= 2 ? W4_DEC(2, 3, 12, 2, 2, 32, 3)
-            : b == 1 ? (k <= 4096 ? W4_DEC(1, 2, 8, 2, 2, 32, 2) : W4_DEC(2, 1, 4, 2, 2, 32, 3))
+            : b == 3 ? W4_DEC(2, 3, 12, 2, 2, 32, 3)
+            : b == 2 ? W4_DEC(2, 2, 8, 2, 2, 32, 3)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 3, 12, 3, 2, 32, 1)
+                        : k == 4096 ? W4_DEC(1, 2, 8, 2, 2, 32, 2)
+                                    : W4_DEC(2, 1, 4, 2, 2, 32, 3))
                      : W4_DEC(2, 1, 4, 2, 2, 32, 2);
         else if (m <= 48)
             b == 4   ? W4_DEC(1, 4, 8, 2, 3, 48, 4)
-            : b >= 2 ? W4_DEC(1, 3, 12, 2, 3, 48, 3)
-            : b == 1 ? W4_DEC(1, 1, 4, 2, 3, 48, 3)
-                     : W4_DEC(1, 1, 4, 2, 3, 48, 2);
+            : b == 3 ? W4_DEC(1, 3, 12, 2, 3, 48, 3)
+            : b == 2 ? W4_DEC(1, 2, 8, 2, 3, 48, 3)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 3, 12, 3, 3, 48, 1) : W4_DEC(1, 1, 4, 2, 3, 48, 3))
+                     : W4_DEC(1, 1, 4, 3, 3, 48, 2);
         else
             b == 4   ? W4_DEC(1, 8, 16, 3, 4, 64, 2)
-            : b >= 2 ? W4_DEC(1, 3, 12, 3, 4, 64, 3)
-            : b == 1 ? W4_DEC(1, 1, 4, 2, 4, 64, 3)
-                     : W4_DEC(1, 1, 4, 2, 4, 64, 2);
+            : b == 3 ? W4_DEC(1, 3, 12, 3, 4, 64, 3)
+            : b == 2 ? W4_DEC(1, 2, 8, 2, 4, 64, 3)
+            : b == 1 ? (k < 4096 ? W4_DEC(1, 3, 12, 3, 4, 64, 1) : W4_DEC(1, 1, 4, 2, 4, 64, 3))
+                     : W4_DEC(1, 1, 4, 3, 4, 64, 2);
     }
 #undef W4_DEC
     return hipGetLastError();
