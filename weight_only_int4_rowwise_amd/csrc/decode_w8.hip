@@ -7,7 +7,11 @@ namespace w4a16 {
 // one-byte codes are the bytes of 256 INT4 indices, so a wave's loads per
 // round stay the same size) and two weight register sets in flight; the
 // tallest GeGLU weights at 16 < m <= 32 take two row groups per wave.  The
-// INT4 shapes would need up to twice the weight registers and spill.
+// INT4 shapes would need up to twice the weight registers and spill.  The
+// tallest GeGLU weights at m <= 4 take one row set of two groups over eight
+// K-parts with two 128-code pieces per chunk (65536 x 12288 on quantized
+// normal codes, alternating with the earlier four-row-set shape through the
+// ABI: 122.1-123.3 against 126.0-127.0 us at m = 1).
 template <bool GEGLU, bool TILED>
 static hipError_t launch_decode_layout8(const void *x, int m, int64_t k, const void *packed,
                                         const void *scales, int64_t n_out, const void *bias,
@@ -23,7 +27,7 @@ static hipError_t launch_decode_layout8(const void *x, int m, int64_t k, const v
     if constexpr (GEGLU) {
         const int b = rows >= 49152 ? 3 : rows >= 24576 ? 2 : rows >= 12288 ? 1 : 0;
         if (m <= 4)
-            b == 3   ? W4_DEC(1, 4, 8, 2, 1, 4, 2)
+            b == 3   ? W4_DEC(2, 1, 8, 2, 1, 4, 2)
             : b == 2 ? W4_DEC(1, 2, 4, 2, 1, 4, 2)
             : b == 1 ? W4_DEC(1, 1, 4, 2, 1, 4, 2)
                      : W4_DEC(1, 1, 8, 2, 1, 4, 2);
