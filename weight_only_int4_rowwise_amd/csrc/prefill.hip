@@ -439,9 +439,11 @@ static hipError_t launch_prefill_layout(const void *x, int64_t m, int64_t k, con
     //  * INT8 codes need a second weight register set per row group, so
     //    their large tiles keep 128 tokens with one row group fewer per
     //    wave: 192 rows (GeGLU: 64 outputs) x 128 tokens, 188-204 VGPRs
-    //    and no spill, where 256 x 128 would spill.  Against 256 x 64
-    //    tiles at m = 2048: attention-out 498 against 559 us, plain FFN-up
-    //    2698 against 3046 us, GeGLU FFN-up 2929 against 3060 us.
+    //    and no spill.  Against 256 x 64 tiles at m = 2048: attention-out
+    //    498 against 559 us, plain FFN-up 2698 against 3046 us, GeGLU
+    //    FFN-up 2929 against 3060 us.  256 x 128 tiles (250 VGPRs, the same
+    //    two waves per SIMD) time the same; split-reduction tiles are
+    //    slower.
     constexpr int out_per = 4 * 16 * (GEGLU ? 2 : 4);
     const int64_t tiles_n = (n_out + out_per - 1) / out_per;
     const int64_t cus = compute_units();
