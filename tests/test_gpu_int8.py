@@ -271,28 +271,3 @@ def test_int8_prefill_geglu(m, f, k):
     qp = w4.w8a16_prepack(q)
     check_geglu(synth.activations(m, k, g), q, s, q_ref, s_ref, f"prefill geglu {m}x{f}x{k}",
                 prepacked=qp)
-
-
-# ------------------------------------------------------ full GLM-130B shape
-
-@pytest.mark.parametrize("m", [1, 8, 64])
-def test_int8_qkv_decode_full(m):
-    """QKV projection 36864 x 12288 in INT8 (prepacked, the layout the
-    benchmark times), every output against the oracle."""
-    g = synth.generator(0, DEV)
-    w = synth.weight(synth.QKV_OUT, synth.HIDDEN, g, device=DEV)
-    announce("int8 QKV quantize")
-    q, s = w4.quantize_rowwise_int8(w)
-    torch.cuda.synchronize()
-    q_ref, s_ref = oracle.quantize_rowwise_int8(bits(w))
-    assert_bits_equal(bits(s), s_ref, "int8 QKV scales")
-    assert_bits_equal(u8(q), q_ref, "int8 QKV codes")
-    del w
-    qp = w4.w8a16_prepack(q)
-    x = synth.activations(m, synth.HIDDEN, g, DEV)
-    announce("int8 QKV decode", m)
-    y = w4.w8a16_linear_prepacked(x, qp, s)
-    torch.cuda.synchronize()
-    y_ref, mag = oracle.linear_int8(bits(x), q_ref, s_ref)
-    r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"int8 QKV M={m}")
-    print(f"int8 QKV M={m}: max err/bound {r:.4f}")

@@ -224,24 +224,3 @@ def test_zp_prefill_geglu(m, f, k):
     g = synth.generator(2600 + m + f)
     qsz = quantize_both(synth.weight(2 * f, k, g, "t4"), f"prefill geglu f={f}")
     check_geglu(synth.activations(m, k, g), qsz, f"prefill geglu {m}x{f}x{k}")
-
-
-@pytest.mark.parametrize("m", [1, 64])
-def test_zp_qkv_decode_full(m):
-    """QKV 36864 x 12288 with zero points, prepacked, every output."""
-    g = synth.generator(0, DEV)
-    w = synth.weight(synth.QKV_OUT, synth.HIDDEN, g, device=DEV)
-    announce("zp QKV quantize")
-    q, s, z = w4.quantize_rowwise_int4_zp(w)
-    torch.cuda.synchronize()
-    p_ref, s_ref, z_ref = oracle.quantize_rowwise_int4_zp(bits(w))
-    assert_bits_equal(bits(s), s_ref, "zp QKV scales")
-    assert_bits_equal(u8(z), z_ref, "zp QKV zero points")
-    assert_bits_equal(u8(q), p_ref, "zp QKV codes")
-    del w
-    x = synth.activations(m, synth.HIDDEN, g, DEV)
-    announce("zp QKV decode", m)
-    y = w4.w4a16_zp_linear_prepacked(x, w4.w4a16_prepack(q), s, z)
-    torch.cuda.synchronize()
-    y_ref, mag = oracle.linear_zp(bits(x), p_ref, s_ref, z_ref)
-    assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"zp QKV M={m}")
