@@ -5,7 +5,9 @@ Inputs are drawn on the GPU (seeded ``torch.Generator('cuda')``; the same
 tensors are copied to the host for the oracle).  Quantized bytes and scales
 are compared in full; decode outputs (m <= 64) in full; two-launch decode
 (m = 100) and prefill outputs (m = 512, 2048) on sampled rows and columns
-that touch every output tile.  The 70-layer decode step runs as the
+that touch every output tile.  Each of these calls also runs on the
+prepacked layout (the one the benchmark times), whose whole output must
+equal the row-major call's bit for bit.  The 70-layer decode step runs as the
 benchmark builds and launches it, and its first and last layers are
 checked in full.
 """
@@ -35,6 +37,14 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
+def _same_bits(y_prepacked, y, what):
+    """Whole outputs of the prepacked and row-major calls, bit for bit
+    (compared on the device)."""
+    torch.cuda.synchronize()
+    differ = int((y_prepacked.view(torch.int16) != y.view(torch.int16)).sum().item())
+    assert differ == 0, f"{what}: {differ} of {y.numel()} outputs differ between the layouts"
+
+
 def _quantize_checked(w, what):
     announce("quantize", what, tuple(w.shape))
     q, s = w4.quantize_rowwise_int4(w)
@@ -50,16 +60,16 @@ def qkv():
     w, xs = synth.qkv_decode(device=DEV)
     q, s, p_ref, s_ref = _quantize_checked(w, "QKV 36864x12288")
     del w
-    return q, s, p_ref, s_ref, xs
+    return q, s, p_ref, s_ref, xs, w4.w4a16_prepack(q)
 
 
 @pytest.mark.parametrize("m", [1, 8, 32, 64])
 def test_qkv_decode_full(qkv, m):
-    q, s, p_ref, s_ref, xs = qkv
+    q, s, p_ref, s_ref, xs, qp = qkv
     x = xs[m]
     announce("QKV decode", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"QKV M={m}")
     y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
     r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
     print(f"QKV M={m}: max err/bound {r:.4f}")
@@ -69,12 +79,12 @@ def test_qkv_two_decode_launches_sampled(qkv):
     """64 < m <= 128 runs the decode kernel on tokens 0..63, then on the
     rest: QKV at m = 100, one token in every 16-token block and two
     columns in every 144-row workgroup tile, against the oracle."""
-    q, s, p_ref, s_ref, _ = qkv
+    q, s, p_ref, s_ref, _, qp = qkv
     m = 100
     x = synth.activations(m, synth.HIDDEN, synth.generator(7, DEV), DEV)
     announce("QKV two decode launches", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"QKV M={m}")
     mi, ni = _sample_indices(m, q.shape[0], 16, 144, 5)
     y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
@@ -86,12 +96,12 @@ def test_qkv_m128_sampled(qkv):
     split over two halves of the workgroup) rather than two decode
     launches: one token in every 16-token block and two columns in every
     192-row tile, against the oracle."""
-    q, s, p_ref, s_ref, _ = qkv
+    q, s, p_ref, s_ref, _, qp = qkv
     m = 128
     x = synth.activations(m, synth.HIDDEN, synth.generator(13, DEV), DEV)
     announce("QKV m=128 GEMM", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"QKV M={m}")
     mi, ni = _sample_indices(m, q.shape[0], 16, 192, 14)
     y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"QKV M={m}")
@@ -103,12 +113,12 @@ def test_qkv_prefill_m1024_sampled(qkv):
     would leave half the CUs idle in its last wave): one token in every
     64-token tile and two columns in every 256-row tile, a quarter of that
     sample against the oracle."""
-    q, s, p_ref, s_ref, _ = qkv
+    q, s, p_ref, s_ref, _, qp = qkv
     m = 1024
     x = synth.activations(m, synth.HIDDEN, synth.generator(8, DEV), DEV)
     announce("QKV prefill", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"QKV prefill M={m}")
     mi, ni = _sample_indices(m, q.shape[0], 64, 256, 9)
     keep = np.random.default_rng(10).random(mi.size) < 0.25
     mi, ni = mi[keep], ni[keep]
@@ -124,16 +134,18 @@ def ffn():
     del w_up
     down = _quantize_checked(w_down, "FFN down 12288x32768 t4")
     del w_down
+    up = (*up, w4.w4a16_prepack(up[0]))
+    down = (*down, w4.w4a16_prepack(down[0]))
     return up, down, x_up, x_down
 
 
 @pytest.mark.parametrize("m", [1, 16])
 def test_geglu_decode_full(ffn, m):
-    (q, s, p_ref, s_ref), _, x_up, _ = ffn
+    (q, s, p_ref, s_ref, qp), _, x_up, _ = ffn
     x = x_up[m]
     announce("GeGLU up decode", m)
     y = w4.w4a16_geglu_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_geglu_linear_prepacked(x, qp, s), y, f"GeGLU up M={m}")
     g, a, b, ma, mb = oracle.geglu(bits(x), p_ref, s_ref)
     r = assert_within(f64(y), g, oracle.geglu_bound(g, a, b, ma, mb), f"GeGLU up M={m}")
     print(f"GeGLU up M={m}: max err/bound {r:.4f}")
@@ -143,12 +155,12 @@ def test_down_prefill_m256_sampled(ffn):
     """FFN-down 12288 x 32768 at m = 256 runs 192-row x 64-token tiles with
     the reduction split over two halves of a 512-thread workgroup: one token
     in every 64-token tile and two columns in every 192-row tile."""
-    _, (q, s, p_ref, s_ref), _, _ = ffn
+    _, (q, s, p_ref, s_ref, qp), _, _ = ffn
     m = 256
     x = synth.activations(m, synth.FFN, synth.generator(11, DEV), DEV)
     announce("FFN-down prefill", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"FFN-down prefill M={m}")
     mi, ni = _sample_indices(m, q.shape[0], 64, 192, 12)
     y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"FFN-down prefill M={m}")
@@ -157,11 +169,11 @@ def test_down_prefill_m256_sampled(ffn):
 
 @pytest.mark.parametrize("m", [1, 16])
 def test_down_decode_full(ffn, m):
-    _, (q, s, p_ref, s_ref), _, x_down = ffn
+    _, (q, s, p_ref, s_ref, qp), _, x_down = ffn
     x = x_down[m]
     announce("FFN down decode", m)
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, f"down M={m}")
     y_ref, mag = oracle.linear(bits(x), p_ref, s_ref)
     r = assert_within(f64(y), y_ref, oracle.linear_bound(mag), f"down M={m}")
     print(f"down M={m}: max err/bound {r:.4f}")
@@ -225,16 +237,18 @@ def prefill_data():
     del w_attn
     up = _quantize_checked(w_up, "FFN up 65536x12288")
     del w_up
+    attn = (*attn, w4.w4a16_prepack(attn[0]))
+    up = (*up, w4.w4a16_prepack(up[0]))
     return attn, up, x
 
 
 def test_prefill_attn_out_sampled(prefill_data):
     """Attention-out at m = 2048: 256-row x 128-token tiles (768 of them,
     a last wave of one workgroup per CU)."""
-    (q, s, p_ref, s_ref), _, x = prefill_data
+    (q, s, p_ref, s_ref, qp), _, x = prefill_data
     announce("prefill attn-out", tuple(x.shape))
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, "prefill attn-out")
     mi, ni = _sample_indices(x.shape[0], q.shape[0], 128, 128, 1)
     y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
     yg = _gather(y, mi, ni)
@@ -247,11 +261,11 @@ def test_prefill_attn_out_m512_sampled(prefill_data):
     (one per CU) with the reduction split over two halves of a 512-thread
     workgroup: one token in every 64-token block and two columns in every
     192-row tile."""
-    (q, s, p_ref, s_ref), _, x = prefill_data
+    (q, s, p_ref, s_ref, qp), _, x = prefill_data
     x5 = x[:512].contiguous()
     announce("prefill attn-out", tuple(x5.shape))
     y = w4.w4a16_linear(x5, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x5, qp, s), y, "prefill attn-out m=512")
     mi, ni = _sample_indices(x5.shape[0], q.shape[0], 64, 192, 6)
     y_ref, mag = oracle.linear_at(bits(x5), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "prefill attn-out m=512")
@@ -263,11 +277,11 @@ def test_attn_out_m96_gemm_sampled(prefill_data):
     launch rather than two decode launches (128-row x 64-token tiles, the
     reduction split over two halves of the workgroup): one token in every
     16-token block and two columns in every 128-row tile."""
-    (q, s, p_ref, s_ref), _, x = prefill_data
+    (q, s, p_ref, s_ref, qp), _, x = prefill_data
     x96 = x[:96].contiguous()
     announce("attn-out m=96 GEMM", tuple(x96.shape))
     y = w4.w4a16_linear(x96, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x96, qp, s), y, "attn-out m=96")
     mi, ni = _sample_indices(x96.shape[0], q.shape[0], 16, 128, 9)
     y_ref, mag = oracle.linear_at(bits(x96), p_ref, s_ref, mi, ni)
     r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), "attn-out m=96")
@@ -275,10 +289,10 @@ def test_attn_out_m96_gemm_sampled(prefill_data):
 
 
 def test_prefill_ffn_up_geglu_sampled(prefill_data):
-    _, (q, s, p_ref, s_ref), x = prefill_data
+    _, (q, s, p_ref, s_ref, qp), x = prefill_data
     announce("prefill FFN-up GeGLU", tuple(x.shape))
     y = w4.w4a16_geglu_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_geglu_linear_prepacked(x, qp, s), y, "prefill FFN-up GeGLU")
     f = q.shape[0] // 2
     mi, ni = _sample_indices(x.shape[0], f, 128, 64, 2)
     g, a, b, ma, mb = oracle.geglu_at(bits(x), p_ref, s_ref, mi, ni)
@@ -288,10 +302,10 @@ def test_prefill_ffn_up_geglu_sampled(prefill_data):
 
 
 def test_prefill_ffn_up_plain_sampled(prefill_data):
-    _, (q, s, p_ref, s_ref), x = prefill_data
+    _, (q, s, p_ref, s_ref, qp), x = prefill_data
     announce("prefill FFN-up plain", tuple(x.shape))
     y = w4.w4a16_linear(x, q, s)
-    torch.cuda.synchronize()
+    _same_bits(w4.w4a16_linear_prepacked(x, qp, s), y, "prefill FFN-up plain")
     mi, ni = _sample_indices(x.shape[0], q.shape[0], 128, 128, 3)
     keep = np.random.default_rng(4).random(mi.size) < 0.25     # a quarter of the sample
     mi, ni = mi[keep], ni[keep]
