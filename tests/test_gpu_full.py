@@ -314,6 +314,38 @@ def test_prefill_ffn_up_plain_sampled(prefill_data):
     print(f"prefill FFN-up plain: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
+@pytest.mark.parametrize("m", [96, 128, 192, 256, 384])
+@pytest.mark.parametrize("weight", ["qkv", "attn_out", "ffn_up_geglu"])
+def test_intermediate_m_sampled(qkv, prefill_data, weight, m):
+    """The benchmark's intermediate token counts on its three weights,
+    prepacked: QKV 36864 x 12288 and the fused FFN-up 65536 x 12288 at
+    m = 96 run two decode launches, attention-out at m = 96 and every
+    weight from m = 128 one GEMM launch with the tile the launch rule
+    picks.  One token in every 32-token block and two columns in every
+    128-row block, a quarter of that sample against the oracle."""
+    if weight == "qkv":
+        _, s, p_ref, s_ref, _, qp = qkv
+    else:
+        _, s, p_ref, s_ref, qp = prefill_data[0 if weight == "attn_out" else 1]
+    geglu = weight == "ffn_up_geglu"
+    n = s.shape[0] // 2 if geglu else s.shape[0]
+    x = synth.activations(m, synth.HIDDEN, synth.generator(40 + m, DEV), DEV)
+    announce("intermediate m", weight, m)
+    fn = w4.w4a16_geglu_linear_prepacked if geglu else w4.w4a16_linear_prepacked
+    y = fn(x, qp, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(m, n, 32, 128, 50 + m)
+    keep = np.random.default_rng(51 + m).random(mi.size) < 0.25
+    mi, ni = mi[keep], ni[keep]
+    if geglu:
+        gr, a, b, ma, mb = oracle.geglu_at(bits(x), p_ref, s_ref, mi, ni)
+        r = assert_within(_gather(y, mi, ni), gr, oracle.geglu_bound(gr, a, b, ma, mb), f"{weight} m={m}")
+    else:
+        y_ref, mag = oracle.linear_at(bits(x), p_ref, s_ref, mi, ni)
+        r = assert_within(_gather(y, mi, ni), y_ref, oracle.linear_bound(mag), f"{weight} m={m}")
+    print(f"{weight} m={m}: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 # ----------------------------------------------------- largest accepted size
 
 def test_largest_accepted_weight():
