@@ -301,6 +301,21 @@ def test_prefill_ffn_up_geglu_sampled(prefill_data):
     print(f"prefill FFN-up GeGLU: {mi.size} sampled outputs, max err/bound {r:.4f}")
 
 
+def test_prefill_ffn_up_geglu_m512_sampled(prefill_data):
+    """The fused FFN-up at m = 512 (128-output x 128-token tiles, 1024 of
+    them), prepacked as the benchmark times it: one token in every 128-token
+    tile and two columns in every 64-output tile."""
+    _, (_, s, p_ref, s_ref, qp), x = prefill_data
+    x5 = x[:512].contiguous()
+    announce("prefill FFN-up GeGLU", tuple(x5.shape))
+    y = w4.w4a16_geglu_linear_prepacked(x5, qp, s)
+    torch.cuda.synchronize()
+    mi, ni = _sample_indices(x5.shape[0], s.shape[0] // 2, 128, 64, 15)
+    g, a, b, ma, mb = oracle.geglu_at(bits(x5), p_ref, s_ref, mi, ni)
+    r = assert_within(_gather(y, mi, ni), g, oracle.geglu_bound(g, a, b, ma, mb), "prefill FFN-up GeGLU m=512")
+    print(f"prefill FFN-up GeGLU m=512: {mi.size} sampled outputs, max err/bound {r:.4f}")
+
+
 def test_prefill_ffn_up_plain_sampled(prefill_data):
     _, (q, s, p_ref, s_ref, qp), x = prefill_data
     announce("prefill FFN-up plain", tuple(x.shape))
