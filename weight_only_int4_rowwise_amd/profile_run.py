@@ -6,6 +6,7 @@ and the summaries made from their output.
     python -m weight_only_int4_rowwise_amd.profile_run step --reps 20
     python -m weight_only_int4_rowwise_amd.profile_run summarize-pmc DIR...
     python -m weight_only_int4_rowwise_amd.profile_run summarize-trace DIR
+    python -m weight_only_int4_rowwise_amd.profile_run step-timeline DIR --after-ms 60
 
 decode   the decode QKV linear (36864 x 12288 INT4 row-wise weights, or INT8
          ones with --codes int8; prepacked or row-major) `reps` times at token
@@ -24,7 +25,11 @@ byte, and its kernel marks the end of the sequence in a trace.
 summarize-pmc reads the counter CSVs of one or more rocprofv3 --pmc runs
 and prints, per kernel, the mean of every counter per dispatch;
 summarize-trace reads a --kernel-trace CSV and prints the per-kernel
-durations and, for the step mode, the gaps between consecutive launches.
+durations and, for the step mode, the gaps between consecutive launches;
+step-timeline reads the --kernel-trace CSV of a step run and prints, over
+the launches that start after --after-ms (past the post-idle clock
+transient), each launch's mean duration and the mean gap from the previous
+launch's end to its start, and the mean step period.
 """
 from __future__ import annotations
 
@@ -249,6 +254,55 @@ def _print_trace(d, sequence=False, by_grid=False):
         prev = e
 
 
+def step_timeline(d, after_ms=60.0, name_part="decode_kernel"):
+    """Launch timeline of a step trace: for every kernel whose name contains
+    name_part and that starts at least after_ms after the first such
+    launch, the mean duration and the mean gap from the previous traced
+    launch's end to its start (us), in launch order of one step; and the
+    mean step period (us), from consecutive starts of the step's first
+    kernel."""
+    seq = [t for t in summarize_trace(d) if name_part in t[0]]
+    if not seq:
+        raise RuntimeError(f"no {name_part} launches in {d}")
+    t0 = seq[0][1]
+    per = OrderedDict()
+    starts = defaultdict(list)
+    prev_end = None
+    for name, st, en in seq:
+        if st - t0 >= after_ms * 1e6 and prev_end is not None:
+            r = per.setdefault(name, {"dur": [], "gap": []})
+            r["dur"].append((en - st) / 1e3)
+            r["gap"].append((st - prev_end) / 1e3)
+            starts[name].append(st)
+        prev_end = en
+    order = []
+    for name, _, _ in seq:                       # the step's launch order
+        if name not in order:
+            order.append(name)
+    per = OrderedDict((name, per[name]) for name in order if name in per)
+    if not per:
+        raise RuntimeError(f"no {name_part} launch starts {after_ms} ms or more into {d}")
+    first = next(iter(per))
+    st0 = starts[first]
+    period = (st0[-1] - st0[0]) / 1e3 / (len(st0) - 1) if len(st0) > 1 else float("nan")
+    rows = [(name, len(v["dur"]), sum(v["dur"]) / len(v["dur"]), sorted(v["dur"])[len(v["dur"]) // 2],
+             sum(v["gap"]) / len(v["gap"])) for name, v in per.items()]
+    return rows, period
+
+
+def _print_timeline(d, after_ms):
+    rows, period = step_timeline(d, after_ms)
+    print(f"launches starting {after_ms:g} ms or more after the first traced decode launch")
+    print("| kernel | launches | mean us | median us | mean gap before it, us |")
+    print("|---|---|---|---|---|")
+    for name, n, mean, med, gap in rows:
+        print(f"| `{name.split('(')[0]}` | {n} | {mean:.2f} | {med:.2f} | {gap:.2f} |")
+    busy = sum(r[2] for r in rows)
+    gaps = sum(r[4] for r in rows)
+    print(f"step period {period:.2f} us = launches {busy:.2f} us + gaps {gaps:.2f} us "
+          f"(+{period - busy - gaps:.2f} us unaccounted)")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -270,6 +324,9 @@ def main(argv=None):
     p.add_argument("dir")
     p.add_argument("--sequence", action="store_true", help="also list every launch in order")
     p.add_argument("--by-grid", action="store_true", help="one line per kernel and grid size")
+    p = sub.add_parser("step-timeline")
+    p.add_argument("dir")
+    p.add_argument("--after-ms", type=float, default=60.0)
     p = sub.add_parser("derived")
     p.add_argument("kernel_part")
     p.add_argument("dirs", nargs="+")
@@ -296,6 +353,9 @@ def main(argv=None):
         return 0
     if a.mode == "summarize-trace":
         _print_trace(a.dir, a.sequence, a.by_grid)
+        return 0
+    if a.mode == "step-timeline":
+        _print_timeline(a.dir, a.after_ms)
         return 0
 
     import torch
